@@ -1,0 +1,67 @@
+"""Build libmedusa.so (all HIP sources under csrc/) for gfx950, in-tree.
+
+Usage: python -m speculative_decoding_heads_amd.build   (or __graft_entry__.build())
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmedusa.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+CFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+    # keep hipcc from forming packed fp32 ops on its own
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+    "-I" + INCLUDE, "-I" + CSRC,
+]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    return obj, r.returncode, out
+
+
+def build(verbose=True, jobs=None):
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    objs = []
+    errors = []
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for obj, rc, out in ex.map(_compile, srcs):
+            objs.append(obj)
+            if out.strip() and verbose:
+                print(out, file=sys.stderr)
+            if rc != 0:
+                errors.append(obj)
+    if errors:
+        raise RuntimeError("HIP compilation failed: " + ", ".join(os.path.basename(e) for e in errors))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,146 @@
+// Candidate expansion and KV compaction.
+//
+// tree_build_candidates follows generate_candidates() and the positions of
+// tree_decoding() on the page "大模型推理 memory bandwidth bound (5) - Medusa"
+// (sections 二.4, 二.5); kv_compact follows update_inference_inputs() (section
+// 二.7), with the tree's K/V read from a side buffer so the copy never overlaps
+// its own source.
+#include "common.h"
+#include "tree_dev.h"
+
+using namespace medusa;
+
+namespace {
+
+// One block per sequence; thread i < T fills node i, threads also fill cart.
+__global__ void candidates_kernel(const medusa_tree_host* __restrict__ t, int H, int K,
+                                  const int32_t* __restrict__ root, const int32_t* __restrict__ topk,
+                                  const int32_t* __restrict__ seq_len, int32_t* __restrict__ tree_tokens,
+                                  int32_t* __restrict__ tree_pos, int32_t* __restrict__ cart) {
+  __shared__ int32_t tok[MEDUSA_MAX_TREE];
+  const int b = blockIdx.x;
+  const int T = t->T, P = t->P, W = t->D + 1;
+  const int tid = threadIdx.x;
+  if (tid < T) {
+    const int fi = t->tree_indices[tid];
+    const int v = fi == 0 ? root[b] : topk[(size_t)b * H * K + (fi - 1)];
+    tok[tid] = v;
+    tree_tokens[(size_t)b * T + tid] = v;
+    tree_pos[(size_t)b * T + tid] = seq_len[b] + t->depth[tid];
+  }
+  __syncthreads();
+  for (int e = tid; e < P * W; e += blockDim.x) {
+    const int p = e / W, j = e % W;
+    const int node = t->retrieve[p * MEDUSA_MAX_TREE + j];
+    cart[(size_t)b * P * W + e] = node >= 0 ? tok[node] : 0;
+  }
+}
+
+// grid (n_layers * Hkv, B, 2 [K or V]); block handles up to D+1 rows of Dh
+// elements with 16-byte moves.  Reads the pre-update seq_len.
+template <int EB>
+__global__ void compact_kv_kernel(const medusa_tree_host* __restrict__ t, int B, int Hkv, int Dh, int64_t Lmax,
+                                  char* __restrict__ Kc, char* __restrict__ Vc, const char* __restrict__ Kt,
+                                  const char* __restrict__ Vt, const int32_t* __restrict__ best,
+                                  const int32_t* __restrict__ accept_len, const int32_t* __restrict__ seq_len,
+                                  const int32_t* __restrict__ n_out, int max_new, int have_out) {
+  const int lh = blockIdx.x;  // layer * Hkv + h
+  const int b = blockIdx.y;
+  const int layer = lh / Hkv, h = lh % Hkv;
+  const int a = accept_len[b];
+  const int s = seq_len[b];
+  const int bi = best[b];
+  if (a < 0 || bi < 0 || bi >= t->P || a + 1 > t->path_len[bi]) return;
+  if ((int64_t)s + a + 1 > Lmax || s < 0) return;
+  if (have_out && (n_out[b] < 0 || n_out[b] + a + 1 > max_new)) return;
+  const int T = t->T;
+  char* dst = blockIdx.z == 0 ? Kc : Vc;
+  const char* src = blockIdx.z == 0 ? Kt : Vt;
+  const size_t row_bytes = (size_t)Dh * EB;
+  const size_t slab = ((size_t)layer * B + b) * Hkv + h;
+  const size_t chunks = row_bytes / 16;
+  for (size_t e = threadIdx.x; e < (size_t)(a + 1) * chunks; e += blockDim.x) {
+    const int i = (int)(e / chunks);
+    const size_t c = e % chunks;
+    const int node = t->retrieve[bi * MEDUSA_MAX_TREE + i];
+    const uint4* sp = (const uint4*)(src + (slab * T + node) * row_bytes) + c;
+    uint4* dp = (uint4*)(dst + (slab * Lmax + s + i) * row_bytes) + c;
+    *dp = *sp;
+  }
+}
+
+// One thread per sequence: append tokens, bump lengths, flag overflow.
+__global__ void compact_finalize_kernel(const medusa_tree_host* __restrict__ t, int B, int64_t Lmax,
+                                        const int32_t* __restrict__ best, const int32_t* __restrict__ accept_len,
+                                        int32_t* __restrict__ seq_len, const int32_t* __restrict__ tree_tokens,
+                                        int32_t* __restrict__ out_tokens, int max_new, int32_t* __restrict__ n_out,
+                                        int32_t* __restrict__ err_flag) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int a = accept_len[b];
+  const int s = seq_len[b];
+  const int bi = best[b];
+  bool bad = a < 0 || bi < 0 || bi >= t->P || a + 1 > t->path_len[bi] || s < 0 || (int64_t)s + a + 1 > Lmax;
+  if (!bad && out_tokens) bad = n_out[b] < 0 || n_out[b] + a + 1 > max_new;
+  if (bad) {
+    if (err_flag) *err_flag = 1;
+    return;
+  }
+  if (out_tokens) {
+    const int n = n_out[b];
+    for (int i = 0; i <= a; ++i)
+      out_tokens[(size_t)b * max_new + n + i] = tree_tokens[(size_t)b * t->T + t->retrieve[bi * MEDUSA_MAX_TREE + i]];
+    n_out[b] = n + a + 1;
+  }
+  seq_len[b] = s + a + 1;
+}
+
+}  // namespace
+
+extern "C" int tree_build_candidates(const medusa_tree* t, int B, int H, int K, const int32_t* root,
+                                     const int32_t* topk_idx, const int32_t* seq_len, int32_t* tree_tokens,
+                                     int32_t* tree_pos, int32_t* cart, hipStream_t stream) {
+  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "tree_build_candidates: null tree");
+  MEDUSA_REQUIRE(B >= 0, MEDUSA_ERR_ARG, "tree_build_candidates: B < 0");
+  MEDUSA_REQUIRE(H >= t->host.D, MEDUSA_ERR_ARG, "tree_build_candidates: H=%d < tree depth %d", H, t->host.D);
+  MEDUSA_REQUIRE(K == t->host.K, MEDUSA_ERR_ARG, "tree_build_candidates: K=%d but the tree uses %d", K,
+                 t->host.K);
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(root && topk_idx && seq_len && tree_tokens && tree_pos && cart, MEDUSA_ERR_ARG,
+                 "tree_build_candidates: null pointer");
+  hipLaunchKernelGGL(candidates_kernel, dim3(B), dim3(64), 0, stream, t->dev, H, K, root, topk_idx, seq_len,
+                     tree_tokens, tree_pos, cart);
+  return check_launch("tree_build_candidates");
+}
+
+extern "C" int kv_compact(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax,
+                          void* Kc, void* Vc, const void* Kt, const void* Vt, const int32_t* best,
+                          const int32_t* accept_len, int32_t* seq_len, const int32_t* tree_tokens,
+                          int32_t* out_tokens, int max_new, int32_t* n_out, int32_t* err_flag,
+                          hipStream_t stream) {
+  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "kv_compact: null tree");
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "kv_compact: dtype %d", dtype);
+  MEDUSA_REQUIRE(n_layers >= 0 && B >= 0 && Hkv > 0 && Dh > 0 && Lmax > 0, MEDUSA_ERR_ARG, "kv_compact: bad sizes");
+  MEDUSA_REQUIRE(((size_t)Dh * dtype_size(dtype)) % 16 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "kv_compact: a K/V row must be a multiple of 16 bytes");
+  MEDUSA_REQUIRE(!out_tokens || (n_out && max_new > 0), MEDUSA_ERR_ARG, "kv_compact: out_tokens needs n_out");
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(best && accept_len && seq_len && tree_tokens, MEDUSA_ERR_ARG, "kv_compact: null pointer");
+  if (n_layers > 0) {
+    MEDUSA_REQUIRE(Kc && Vc && Kt && Vt, MEDUSA_ERR_ARG, "kv_compact: null K/V pointer");
+    dim3 grid(n_layers * Hkv, B, 2);
+    if (dtype == MEDUSA_BF16)
+      hipLaunchKernelGGL(compact_kv_kernel<2>, grid, dim3(128), 0, stream, t->dev, B, Hkv, Dh, Lmax, (char*)Kc,
+                         (char*)Vc, (const char*)Kt, (const char*)Vt, best, accept_len, seq_len, n_out, max_new,
+                         out_tokens != nullptr);
+    else
+      hipLaunchKernelGGL(compact_kv_kernel<4>, grid, dim3(128), 0, stream, t->dev, B, Hkv, Dh, Lmax, (char*)Kc,
+                         (char*)Vc, (const char*)Kt, (const char*)Vt, best, accept_len, seq_len, n_out, max_new,
+                         out_tokens != nullptr);
+    int rc = check_launch("kv_compact");
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(compact_finalize_kernel, dim3((B + 63) / 64), dim3(64), 0, stream, t->dev, B, Lmax, best,
+                     accept_len, seq_len, tree_tokens, out_tokens, max_new, n_out, err_flag);
+  return check_launch("kv_compact finalize");
+}

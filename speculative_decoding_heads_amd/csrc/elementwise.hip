@@ -1,0 +1,202 @@
+// Row-wise kernels of the verify forward: RMSNorm, rotary split of the fused
+// Q/K/V projection into the query tensor and the tree K/V side buffers,
+// embedding gather, row gather (the selected node's hidden state, which the
+// page "大模型推理 memory bandwidth bound (5) - Medusa" hands to the next round's
+// heads in section 二.7) and row argmax (the greedy root of section 二.4).
+#include "common.h"
+#include "medusa_model.h"
+
+using namespace medusa;
+
+namespace {
+
+// one block (256 threads) per row
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(int N, const T* __restrict__ x, const T* __restrict__ w,
+                                                      float eps, T* __restrict__ y) {
+  const int m = blockIdx.x;
+  const T* xr = x + (size_t)m * N;
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int n = threadIdx.x; n < N; n += 256) {
+    const float v = Elem<T>::load(xr, n);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+  for (int n = threadIdx.x; n < N; n += 256)
+    Elem<T>::store(y, (size_t)m * N + n, Elem<T>::load(xr, n) * inv * Elem<T>::load(w, n));
+}
+
+// grid (B*T, Hq + 2*Hkv), block Dh/2 threads (pairs i, i + Dh/2)
+template <typename T>
+__global__ void rope_split_kernel(int T_, int Hq, int Hkv, int Dh, const float* __restrict__ qkv,
+                                  const int32_t* __restrict__ pos, const float* __restrict__ ct,
+                                  const float* __restrict__ st, int max_pos, T* __restrict__ q_out, T* __restrict__ Kt,
+                                  T* __restrict__ Vt) {
+  const int row = blockIdx.x;  // b*T + t
+  const int head = blockIdx.y;
+  const int b = row / T_, t = row % T_;
+  const int half = Dh / 2;
+  const int W = (Hq + 2 * Hkv) * Dh;
+  const float* src = qkv + (size_t)row * W + (size_t)head * Dh;
+  int p = pos[row];
+  p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) {
+    const float x1 = src[i], x2 = src[i + half];
+    if (head < Hq + Hkv) {
+      const float c = ct[(size_t)p * half + i], s = st[(size_t)p * half + i];
+      const float y1 = x1 * c - x2 * s;
+      const float y2 = x2 * c + x1 * s;
+      if (head < Hq) {
+        T* d = q_out + ((size_t)row * Hq + head) * Dh;
+        Elem<T>::store(d, i, y1);
+        Elem<T>::store(d, i + half, y2);
+      } else {
+        const int h = head - Hq;
+        T* d = Kt + (((size_t)b * Hkv + h) * T_ + t) * Dh;
+        Elem<T>::store(d, i, y1);
+        Elem<T>::store(d, i + half, y2);
+      }
+    } else {
+      const int h = head - Hq - Hkv;
+      T* d = Vt + (((size_t)b * Hkv + h) * T_ + t) * Dh;
+      Elem<T>::store(d, i, x1);
+      Elem<T>::store(d, i + half, x2);
+    }
+  }
+}
+
+template <typename T>
+__global__ void embed_kernel(int d, const int32_t* __restrict__ tok, const T* __restrict__ table, int V,
+                             T* __restrict__ out) {
+  const int m = blockIdx.x;
+  int v = tok[m];
+  v = v < 0 ? 0 : (v >= V ? V - 1 : v);
+  for (int n = threadIdx.x; n < d; n += blockDim.x) out[(size_t)m * d + n] = table[(size_t)v * d + n];
+}
+
+template <typename T>
+__global__ void gather_rows_kernel(int T_, int d, const T* __restrict__ h, const int32_t* __restrict__ sel,
+                                   T* __restrict__ out) {
+  const int b = blockIdx.x;
+  int s = sel[b];
+  s = s < 0 ? 0 : (s >= T_ ? T_ - 1 : s);
+  for (int n = threadIdx.x; n < d; n += blockDim.x) out[(size_t)b * d + n] = h[((size_t)b * T_ + s) * d + n];
+}
+
+__global__ __launch_bounds__(256) void argmax_rows_kernel(int V, const float* __restrict__ x, int64_t ldx,
+                                                          int32_t* __restrict__ out) {
+  const int m = blockIdx.x;
+  const float* r = x + (size_t)m * ldx;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int k = threadIdx.x; k < V; k += 256) {
+    const float v = r[k];
+    if (v > bv) {
+      bv = v;
+      bi = k;
+    }
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    if (v2 > bv || (v2 == bv && i2 < bi)) {
+      bv = v2;
+      bi = i2;
+    }
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = bv;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int j = 1; j < 4; ++j)
+      if (sv[j] > bv || (sv[j] == bv && si[j] < bi)) {
+        bv = sv[j];
+        bi = si[j];
+      }
+    out[m] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+}  // namespace
+
+extern "C" int medusa_rmsnorm(int dtype, int M, int N, const void* x, const void* w, float eps, void* y,
+                              hipStream_t stream) {
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "rmsnorm: dtype");
+  MEDUSA_REQUIRE(M >= 0 && N > 0, MEDUSA_ERR_ARG, "rmsnorm: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(x && w && y, MEDUSA_ERR_ARG, "rmsnorm: null pointer");
+  if (dtype == MEDUSA_F32)
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, stream, N, (const float*)x, (const float*)w, eps,
+                       (float*)y);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, N, (const bf16_t*)x, (const bf16_t*)w,
+                       eps, (bf16_t*)y);
+  return check_launch("rmsnorm");
+}
+
+extern "C" int medusa_rope_split(int dtype, int B, int T, int Hq, int Hkv, int Dh, const float* qkv,
+                                 const int32_t* pos, const float* cos_tab, const float* sin_tab, int max_pos,
+                                 void* q_out, void* Kt, void* Vt, hipStream_t stream) {
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "rope_split: dtype");
+  MEDUSA_REQUIRE(B >= 0 && T > 0 && Hq > 0 && Hkv > 0 && Dh > 0 && Dh % 2 == 0 && max_pos > 0, MEDUSA_ERR_ARG,
+                 "rope_split: bad sizes");
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(qkv && pos && cos_tab && sin_tab && q_out && Kt && Vt, MEDUSA_ERR_ARG, "rope_split: null pointer");
+  dim3 grid(B * T, Hq + 2 * Hkv);
+  const int thr = Dh / 2 < 64 ? 64 : (Dh / 2 > 256 ? 256 : Dh / 2);
+  if (dtype == MEDUSA_F32)
+    hipLaunchKernelGGL(rope_split_kernel<float>, grid, dim3(thr), 0, stream, T, Hq, Hkv, Dh, qkv, pos, cos_tab,
+                       sin_tab, max_pos, (float*)q_out, (float*)Kt, (float*)Vt);
+  else
+    hipLaunchKernelGGL(rope_split_kernel<bf16_t>, grid, dim3(thr), 0, stream, T, Hq, Hkv, Dh, qkv, pos, cos_tab,
+                       sin_tab, max_pos, (bf16_t*)q_out, (bf16_t*)Kt, (bf16_t*)Vt);
+  return check_launch("rope_split");
+}
+
+extern "C" int medusa_embed(int dtype, int M, int d, const int32_t* tokens, const void* table, int V, void* out,
+                            hipStream_t stream) {
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "embed: dtype");
+  MEDUSA_REQUIRE(M >= 0 && d > 0 && V > 0, MEDUSA_ERR_ARG, "embed: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(tokens && table && out, MEDUSA_ERR_ARG, "embed: null pointer");
+  if (dtype == MEDUSA_F32)
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, stream, d, tokens, (const float*)table, V,
+                       (float*)out);
+  else
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, d, tokens, (const bf16_t*)table, V,
+                       (bf16_t*)out);
+  return check_launch("embed");
+}
+
+extern "C" int medusa_gather_rows(int dtype, int B, int T, int d, const void* h, const int32_t* sel, void* out,
+                                  hipStream_t stream) {
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "gather_rows: dtype");
+  MEDUSA_REQUIRE(B >= 0 && T > 0 && d > 0, MEDUSA_ERR_ARG, "gather_rows: bad sizes");
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(h && sel && out, MEDUSA_ERR_ARG, "gather_rows: null pointer");
+  if (dtype == MEDUSA_F32)
+    hipLaunchKernelGGL(gather_rows_kernel<float>, dim3(B), dim3(256), 0, stream, T, d, (const float*)h, sel,
+                       (float*)out);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<bf16_t>, dim3(B), dim3(256), 0, stream, T, d, (const bf16_t*)h, sel,
+                       (bf16_t*)out);
+  return check_launch("gather_rows");
+}
+
+extern "C" int medusa_argmax_rows(int M, int V, const float* x, int64_t ldx, int32_t* out, hipStream_t stream) {
+  MEDUSA_REQUIRE(M >= 0 && V > 0 && ldx >= V, MEDUSA_ERR_ARG, "argmax_rows: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(x && out, MEDUSA_ERR_ARG, "argmax_rows: null pointer");
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(M), dim3(256), 0, stream, V, x, ldx, out);
+  return check_launch("argmax_rows");
+}

@@ -1,0 +1,204 @@
+// Acceptance and longest-path selection.
+//
+// Follows evaluate_posterior() on the page "大模型推理 memory bandwidth bound (5)
+// - Medusa" (section 二.6) and the typical-acceptance rule of section 一.3.  The
+// page evaluates every root-to-leaf path on a [paths, depth, V] copy of the
+// logits; here the per-node statistics are computed once per tree node (each
+// node's logits are read from memory once per pass), and one lane per path then
+// walks its path.
+//
+//   pass A, grid (T, B): per node u -- argmax (lowest index on ties); for
+//     typical also max, Z = sum exp((x-max)/tau) and
+//     H = -sum q log(q + 1e-5) with q = exp((x-max)/tau)/Z, threshold
+//     thr = min(eps, delta*exp(-H)).
+//   pass B, grid (B): lane p walks path p, counts leading accepted candidates
+//     (pads never accepted), sums log q for typical; a wave reduction picks
+//     the accept length, the best path, the selected node and the next root.
+#include "common.h"
+#include "tree_dev.h"
+
+using namespace medusa;
+
+namespace {
+
+struct NodeStat {
+  int32_t amax;
+  float m, Z, thr;
+};
+
+constexpr int kStatThreads = 256;
+
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+__global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* __restrict__ logits, int T, int V,
+                                                                 int typical, float inv_tau, float eps, float delta,
+                                                                 NodeStat* __restrict__ out) {
+  const int u = blockIdx.x, b = blockIdx.y;
+  const float* x = logits + ((size_t)b * T + u) * V;
+  const int tid = threadIdx.x;
+  __shared__ float s_v[kStatThreads / 64];
+  __shared__ int s_i[kStatThreads / 64];
+  __shared__ float s_f[kStatThreads / 64];
+  const int lane = tid & 63, w = tid >> 6;
+
+  // argmax / max
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int k = tid; k < V; k += kStatThreads) {
+    const float v = x[k];
+    if (v > bv) {  // strictly greater keeps the lowest index of this thread's stripe
+      bv = v;
+      bi = k;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o, 64);
+    const int i2 = __shfl_xor(bi, o, 64);
+    argmax_merge(bv, bi, v2, i2);
+  }
+  if (lane == 0) {
+    s_v[w] = bv;
+    s_i[w] = bi;
+  }
+  __syncthreads();
+  bv = s_v[0];
+  bi = s_i[0];
+  for (int j = 1; j < kStatThreads / 64; ++j) argmax_merge(bv, bi, s_v[j], s_i[j]);
+  if (bi == 0x7fffffff) bi = 0;  // all NaN row: report token 0
+  if (!typical) {
+    if (tid == 0) out[(size_t)b * T + u] = NodeStat{bi, bv, 0.f, 0.f};
+    return;
+  }
+  const float m = bv;
+  // Z = sum exp((x - m)/tau)
+  float z = 0.f;
+  for (int k = tid; k < V; k += kStatThreads) z += expf((x[k] - m) * inv_tau);
+  z = wave_sum(z);
+  __syncthreads();
+  if (lane == 0) s_f[w] = z;
+  __syncthreads();
+  float Z = 0.f;
+  for (int j = 0; j < kStatThreads / 64; ++j) Z += s_f[j];
+  const float invZ = 1.0f / Z;
+  // H = -sum q log(q + 1e-5)
+  float hsum = 0.f;
+  for (int k = tid; k < V; k += kStatThreads) {
+    const float q = expf((x[k] - m) * inv_tau) * invZ;
+    hsum += q * logf(q + 1e-5f);
+  }
+  hsum = wave_sum(hsum);
+  __syncthreads();
+  if (lane == 0) s_f[w] = hsum;
+  __syncthreads();
+  if (tid == 0) {
+    float hs = 0.f;
+    for (int j = 0; j < kStatThreads / 64; ++j) hs += s_f[j];
+    const float H = -hs;
+    const float thr = fminf(eps, delta * expf(-H));
+    out[(size_t)b * T + u] = NodeStat{bi, m, Z, thr};
+  }
+}
+
+// One wave per sequence, lane p = path p (P <= 64).
+__global__ __launch_bounds__(64) void select_kernel(const medusa_tree_host* __restrict__ t, const float* __restrict__ logits,
+                                                    int V, const int32_t* __restrict__ tree_tokens, int typical,
+                                                    float inv_tau, const NodeStat* __restrict__ st,
+                                                    int32_t* __restrict__ best_out, int32_t* __restrict__ acc_out,
+                                                    int32_t* __restrict__ sel_out, int32_t* __restrict__ root_out) {
+  const int b = blockIdx.x;
+  const int p = threadIdx.x;
+  const int T = t->T, P = t->P;
+  const NodeStat* s = st + (size_t)b * T;
+  int acc = -1;  // lanes without a path never win
+  float lik = -INFINITY;
+  if (p < P) {
+    acc = 0;
+    lik = 0.f;
+    const int len = t->path_len[p];
+    const int32_t* row = t->retrieve + p * MEDUSA_MAX_TREE;
+    for (int j = 1; j < len; ++j) {
+      const int u = row[j - 1];
+      const int tok = tree_tokens[(size_t)b * T + row[j]];
+      bool ok;
+      if (!typical) {
+        ok = tok == s[u].amax;
+      } else {
+        float q = 0.f;
+        if (tok >= 0 && tok < V) q = expf((logits[((size_t)b * T + u) * V + tok] - s[u].m) * inv_tau) / s[u].Z;
+        ok = q > s[u].thr;
+        if (ok) lik += logf(q);
+      }
+      if (!ok) break;
+      ++acc;
+    }
+  }
+  // a = max acc
+  int a = acc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a = max(a, __shfl_xor(a, o, 64));
+  int best = 0;
+  if (a > 0) {
+    const bool cand = acc == a;
+    if (!typical) {
+      const uint64_t m = __ballot(cand);
+      best = __ffsll((unsigned long long)m) - 1;
+    } else {
+      float l = cand ? lik : -INFINITY;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) l = fmaxf(l, __shfl_xor(l, o, 64));
+      const uint64_t m = __ballot(cand && lik == l);
+      best = __ffsll((unsigned long long)m) - 1;
+    }
+  } else {
+    a = 0;
+  }
+  if (p == 0) {
+    const int sel = t->retrieve[best * MEDUSA_MAX_TREE + a];
+    best_out[b] = best;
+    acc_out[b] = a;
+    sel_out[b] = sel;
+    root_out[b] = s[sel].amax;
+  }
+}
+
+}  // namespace
+
+extern "C" size_t evaluate_posterior_workspace_size(int B, int T) {
+  if (B <= 0 || T <= 0) return 0;
+  return align_up((size_t)B * T * sizeof(NodeStat), 256);
+}
+
+extern "C" int evaluate_posterior(const medusa_tree* t, int B, int V, const float* logits, const int32_t* tree_tokens,
+                                  int mode, float temperature, float eps, float delta, int32_t* best,
+                                  int32_t* accept_len, int32_t* sel_node, int32_t* next_root, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "evaluate_posterior: null tree");
+  MEDUSA_REQUIRE(B >= 0 && V > 0, MEDUSA_ERR_ARG, "evaluate_posterior: bad sizes");
+  MEDUSA_REQUIRE(mode == MEDUSA_GREEDY || mode == MEDUSA_TYPICAL, MEDUSA_ERR_ARG, "evaluate_posterior: mode %d",
+                 mode);
+  MEDUSA_REQUIRE(mode == MEDUSA_GREEDY || temperature > 0.f, MEDUSA_ERR_ARG,
+                 "evaluate_posterior: typical acceptance needs temperature > 0");
+  MEDUSA_REQUIRE(t->host.P <= 64, MEDUSA_ERR_UNSUPPORTED, "evaluate_posterior: more than 64 paths");
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(logits && tree_tokens && best && accept_len && sel_node && next_root, MEDUSA_ERR_ARG,
+                 "evaluate_posterior: null pointer");
+  const int T = t->host.T;
+  MEDUSA_REQUIRE(ws && ws_bytes >= evaluate_posterior_workspace_size(B, T), MEDUSA_ERR_WORKSPACE,
+                 "evaluate_posterior: workspace %zu < %zu", ws_bytes, evaluate_posterior_workspace_size(B, T));
+  NodeStat* st = (NodeStat*)ws;
+  const int typical = mode == MEDUSA_TYPICAL;
+  const float inv_tau = typical ? 1.0f / temperature : 1.0f;
+  hipLaunchKernelGGL(node_stats_kernel, dim3(T, B), dim3(kStatThreads), 0, stream, logits, T, V, typical, inv_tau,
+                     eps, delta, st);
+  int rc = check_launch("evaluate_posterior stats");
+  if (rc) return rc;
+  hipLaunchKernelGGL(select_kernel, dim3(B), dim3(64), 0, stream, t->dev, logits, V, tree_tokens, typical, inv_tau,
+                     st, best, accept_len, sel_node, next_root);
+  return check_launch("evaluate_posterior select");
+}

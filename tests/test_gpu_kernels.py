@@ -1,0 +1,264 @@
+"""GPU parity of the other verify-step calls against the oracle: candidates,
+acceptance, KV compaction, Medusa heads + top-K, and the product epilogues.
+
+Integer outputs (indices, accept lengths, tokens, copied rows) must be bit-exact.
+Acceptance is checked on identical logits; the typical rule takes its decisions
+in float32 on both sides and a decision whose probability lies within 1e-5
+(relative) of its threshold may go either way (such near-ties are counted)."""
+import numpy as np
+import pytest
+
+from oracle.candidates import build_candidates
+from oracle.heads import medusa_heads_logits, topk_desc
+from oracle.numerics import silu
+from oracle.posterior import GREEDY, TYPICAL, evaluate_posterior_one
+from oracle.tree import tree_buffers
+from oracle.update import kv_compact as oracle_compact
+from workloads import PAGE_TREE_CHOICES, TWO_HEAD_CHOICES, heads_weights, seeded_tree_choices
+
+from _gpu import assert_close, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+TREES = [PAGE_TREE_CHOICES, seeded_tree_choices(0), TWO_HEAD_CHOICES, [(0,), (1,), (0, 0)]]
+
+
+@pytest.mark.parametrize("ti", range(len(TREES)))
+def test_candidates_bit_exact(dev, ti):
+    import torch
+    from speculative_decoding_heads_amd import api
+    choices = TREES[ti]
+    say("tree_build_candidates tree", ti)
+    tree = api.Tree(choices)
+    ot = tree_buffers(choices)
+    rng = np.random.default_rng(ti)
+    B, H = 5, ot["D"] + 1
+    root = rng.integers(0, 32000, B).astype(np.int32)
+    topk = rng.integers(0, 32000, (B, H, ot["K"])).astype(np.int32)
+    seq = rng.integers(0, 5000, B).astype(np.int32)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    tok, pos, cart = api.tree_build_candidates(tree, d(root), d(topk), d(seq))
+    torch.cuda.synchronize()
+    rt, rp, rc = build_candidates(ot, root, topk, seq)
+    assert np.array_equal(to_np(tok), rt) and np.array_equal(to_np(pos), rp) and np.array_equal(to_np(cart), rc)
+
+
+def _posterior_case(rng, ot, B, V, mode, match_p=0.7, scale=3.0):
+    T = ot["T"]
+    lg = (rng.standard_normal((B, T, V)) * scale).astype(np.float32)
+    toks = rng.integers(0, V, (B, T)).astype(np.int32)
+    for b in range(B):
+        amax = lg[b].argmax(1)
+        for c in range(1, T):
+            if rng.uniform() < match_p:
+                toks[b, c] = amax[ot["parent"][c]]
+    return lg, toks
+
+
+@pytest.mark.parametrize("ti", range(len(TREES)))
+@pytest.mark.parametrize("mode", [GREEDY, TYPICAL])
+def test_posterior_bit_exact(dev, ti, mode):
+    import torch
+    from speculative_decoding_heads_amd import api
+    choices = TREES[ti]
+    tree = api.Tree(choices)
+    ot = tree_buffers(choices)
+    rng = np.random.default_rng(100 + ti + 10 * mode)
+    near = 0
+    for V, scale in [(512, 3.0), (32000, 1.0)]:
+        say("evaluate_posterior tree", ti, "mode", mode, "V", V)
+        B = 6
+        lg, toks = _posterior_case(rng, ot, B, V, mode, scale=scale)
+        tau, eps, delta = 0.7, 0.09, 0.3
+        best, a, sel, nr = api.evaluate_posterior(tree, torch.from_numpy(lg).to(dev), torch.from_numpy(toks).to(dev),
+                                                  mode, tau, eps, delta)
+        torch.cuda.synchronize()
+        got = np.stack([to_np(x) for x in (best, a, sel, nr)], 1)
+        for b in range(B):
+            r = evaluate_posterior_one(ot, lg[b], toks[b], mode, tau, eps, delta)
+            ref = (r["best"], r["accept_len"], r["sel"], r["next_root"])
+            if tuple(got[b]) != ref:
+                close = [m for k, m in r["margins"] if k != "argmax_gap" and m < 1e-5]
+                assert close, "posterior mismatch b=%d got %s ref %s" % (b, got[b], ref)
+                near += 1
+    assert near <= 1
+
+
+def test_posterior_typical_extremes(dev):
+    """eps = 0 accepts every candidate; a threshold above 1 accepts none (special cases of the rule)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("evaluate_posterior extremes")
+    ot = tree_buffers(PAGE_TREE_CHOICES)
+    tree = api.Tree(PAGE_TREE_CHOICES)
+    rng = np.random.default_rng(7)
+    lg = rng.standard_normal((2, 64, 1000)).astype(np.float32)
+    toks = rng.integers(0, 1000, (2, 64)).astype(np.int32)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    best, a, sel, nr = api.evaluate_posterior(tree, d(lg), d(toks), TYPICAL, 0.7, 0.0, 0.3)
+    torch.cuda.synchronize()
+    assert to_np(a).tolist() == [4, 4]
+    for b in range(2):
+        r = evaluate_posterior_one(ot, lg[b], toks[b], TYPICAL, 0.7, 0.0, 0.3)
+        assert (int(to_np(best)[b]), int(to_np(sel)[b])) == (r["best"], r["sel"])
+    best, a, sel, nr = api.evaluate_posterior(tree, d(lg), d(toks), TYPICAL, 0.7, 2.0, 1e6)
+    torch.cuda.synchronize()
+    assert to_np(a).tolist() == [0, 0] and to_np(best).tolist() == [0, 0] and to_np(sel).tolist() == [0, 0]
+    assert to_np(nr).tolist() == lg[:, 0].argmax(1).tolist()
+
+
+@pytest.mark.parametrize("dtype_name", ["bf16", "fp32"])
+def test_kv_compact_bit_exact(dev, dtype_name):
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("kv_compact", dtype_name)
+    tdt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    ot = tree_buffers(PAGE_TREE_CHOICES)
+    tree = api.Tree(PAGE_TREE_CHOICES)
+    rng = np.random.default_rng(3)
+    NL, B, Hkv, Lmax, Dh, T = 3, 4, 2, 50, 64, 64
+    Kc = rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32)
+    Vc = rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32)
+    Kt = rng.standard_normal((NL, B, Hkv, T, Dh)).astype(np.float32)
+    Vt = rng.standard_normal((NL, B, Hkv, T, Dh)).astype(np.float32)
+    if dtype_name == "bf16":
+        from workloads import bf16_round
+        Kc, Vc, Kt, Vt = (bf16_round(x) for x in (Kc, Vc, Kt, Vt))
+    best = np.array([0, 7, 41, 20], np.int32)
+    acc = np.array([4, 3, 0, 2], np.int32)  # within each chosen path's length
+    seq = np.array([10, 40, 49, 0], np.int32)
+    toks = rng.integers(0, 1000, (B, T)).astype(np.int32)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    gK, gV = to_dev(Kc, tdt, dev), to_dev(Vc, tdt, dev)
+    gseq = d(seq)
+    out_tokens = torch.full((B, 16), -1, dtype=torch.int32, device=dev)
+    n_out = torch.tensor([0, 3, 16, 1], dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    api.kv_compact(tree, gK, gV, to_dev(Kt, tdt, dev), to_dev(Vt, tdt, dev), d(best), d(acc), gseq, d(toks),
+                   out_tokens, n_out, err)
+    torch.cuda.synchronize()
+    # sequence 2 (seq 49 + 1 > 50 would fit, n_out 16 + 1 > 16 does not) must be untouched and flagged
+    rK, rV, rseq = oracle_compact(ot, Kc, Vc, Kt, Vt, best, acc, seq)
+    rseq[2] = seq[2]
+    rK[:, 2], rV[:, 2] = Kc[:, 2], Vc[:, 2]
+    assert np.array_equal(to_np(gK), rK) and np.array_equal(to_np(gV), rV)
+    assert to_np(gseq).tolist() == rseq.tolist()
+    assert int(to_np(err)[0]) == 1
+    ot_ = to_np(out_tokens)
+    for b, n0 in [(0, 0), (1, 3), (3, 1)]:
+        want = [int(toks[b, ot["retrieve"][best[b], i]]) for i in range(acc[b] + 1)]
+        assert ot_[b, n0:n0 + acc[b] + 1].tolist() == want
+    assert to_np(n_out).tolist() == [5, 7, 16, 4]
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_heads_topk_bf16_full_size(dev, B):
+    """Medusa heads at d 4096, V 32000, 4 heads, top-10 (bf16): logits at the returned
+    indices match the oracle; indices bit-exact except where the oracle's own ranking
+    has a near-tie at the error level."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("medusa_heads_topk bf16 B", B)
+    h, W1, W2 = heads_weights(seed=B, B=B)
+    tdt = torch.bfloat16
+    idx, val = api.medusa_heads_topk(to_dev(h, tdt, dev), to_dev(W1, tdt, dev), to_dev(W2, tdt, dev), 10)
+    torch.cuda.synchronize()
+    # the ranking is decided on float32 logits on both sides
+    ref_logits = medusa_heads_logits(h, W1, W2, bf16=True).astype(np.float32).astype(np.float64)
+    gi, gv = to_np(idx), to_np(val)
+    ref_idx = topk_desc(ref_logits, 10)
+    err = 0.0
+    for b in range(B):
+        for k in range(4):
+            rl = ref_logits[b, k]
+            assert_close(gv[b, k], rl[gi[b, k]], rtol=2e-2, atol=1e-2, what="topk values")
+            err = max(err, float(np.abs(gv[b, k] - rl[gi[b, k]]).max()))
+    mism = 0
+    for b in range(B):
+        for k in range(4):
+            if gi[b, k].tolist() != ref_idx[b, k].tolist():
+                # allowed only where the reference ranking has a gap below the measured error
+                kth = np.sort(ref_logits[b, k])[::-1]
+                gap = np.min(np.abs(np.diff(kth[:11])))
+                assert gap <= 4 * err + 1e-7, "top-K mismatch without near-tie (b=%d k=%d)" % (b, k)
+                mism += 1
+    assert mism <= B
+
+
+def test_heads_topk_fp32_small(dev):
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("medusa_heads_topk fp32 small")
+    rng = np.random.default_rng(0)
+    h = rng.standard_normal((3, 64)).astype(np.float32)
+    W1 = (rng.standard_normal((2, 64, 64)) * 0.02).astype(np.float32)
+    W2 = (rng.standard_normal((2, 512, 64)) * 0.02).astype(np.float32)
+    idx, val = api.medusa_heads_topk(*(torch.from_numpy(x).to(dev) for x in (h, W1, W2)), 3)
+    torch.cuda.synchronize()
+    ref = medusa_heads_logits(h, W1, W2)
+    assert np.array_equal(to_np(idx), topk_desc(ref, 3))
+    assert_close(to_np(val), np.take_along_axis(ref, topk_desc(ref, 3), -1), rtol=1e-5, atol=1e-6, what="val")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (8, 1000, 512), (64, 12288, 4096), (64, 4096, 11008),
+                                   (100, 384, 256), (512, 512, 4096)])
+def test_gemm_bf16(dev, M, N, K):
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import EPI_F32
+    say("gemm bf16", M, N, K)
+    rng = np.random.default_rng(M + N)
+    from workloads import bf16_round
+    A = bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    W = bf16_round((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    out = api.gemm(to_dev(A, torch.bfloat16, dev), to_dev(W, torch.bfloat16, dev), EPI_F32)
+    torch.cuda.synchronize()
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    assert_close(to_np(out), ref, rtol=1e-4, atol=1e-4, what="gemm")
+
+
+@pytest.mark.parametrize("dtype_name", ["bf16", "fp32"])
+def test_gemm_epilogues(dev, dtype_name):
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import EPI_RESID, EPI_SILU_RESID_A, EPI_STORE, EPI_SWIGLU
+    from workloads import bf16_round
+    say("gemm epilogues", dtype_name)
+    tdt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    rnd = bf16_round if dtype_name == "bf16" else (lambda x: x)
+    tol = dict(rtol=2e-2, atol=1e-2) if dtype_name == "bf16" else dict(rtol=1e-5, atol=1e-5)
+    rng = np.random.default_rng(1)
+    M, K = 5, 256
+    A = rnd(rng.standard_normal((M, K)).astype(np.float32))
+    W = rnd((rng.standard_normal((512, K)) * 0.05).astype(np.float32))
+    R = rnd(rng.standard_normal((M, 512)).astype(np.float32))
+    acc = A.astype(np.float64) @ W.astype(np.float64).T
+    gA, gW = to_dev(A, tdt, dev), to_dev(W, tdt, dev)
+    out = api.gemm(gA, gW, EPI_STORE)
+    assert_close(to_np(out), acc, what="store", **tol)
+    gR = to_dev(R, tdt, dev)
+    out = api.gemm(gA, gW, EPI_RESID, out=gR.clone(), R=gR)
+    assert_close(to_np(out), acc + R, what="resid", **tol)
+    out = api.gemm(gA, gW, EPI_SWIGLU)
+    assert_close(to_np(out), silu(acc[:, 0::2]) * acc[:, 1::2], what="swiglu", **tol)
+    Wsq = rnd((rng.standard_normal((2 * K, K)) * 0.05).astype(np.float32))  # two K x K heads stacked
+    out = api.gemm(gA, to_dev(Wsq, tdt, dev), EPI_SILU_RESID_A)
+    z = A.astype(np.float64) @ Wsq.astype(np.float64).T
+    assert_close(to_np(out), np.concatenate([A, A], 1) + silu(z), what="silu_resid", **tol)
+    torch.cuda.synchronize()
+
+
+def test_argmax_and_topk_rows_ties(dev):
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("argmax/topk rows")
+    x = np.zeros((3, 1000), np.float32)
+    x[0, [5, 17, 900]] = 2.0
+    x[1] = np.random.default_rng(0).standard_normal(1000)
+    x[2, 999] = 1.0
+    g = torch.from_numpy(x).to(dev)
+    am = api.argmax_rows(g)
+    idx, val = api.topk_rows(g, 5)
+    torch.cuda.synchronize()
+    assert to_np(am).tolist() == [5, int(x[1].argmax()), 999]
+    assert np.array_equal(to_np(idx), topk_desc(x, 5))
