@@ -68,8 +68,10 @@ int medusa_gather_rows(int dtype, int B, int T, int d, const void* h, const int3
 /* out[m] = argmax_v x[m*ldx + v] (lowest index on ties) for fp32 rows */
 int medusa_argmax_rows(int M, int V, const float* x, int64_t ldx, int32_t* out, hipStream_t stream);
 
-/* Top-K of fp32 rows: idx/val [M, K], value-descending, ties -> lower index; K <= 16 */
-int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* idx, float* val, hipStream_t stream);
+/* Top-K of fp32 rows: idx/val [M, K] (val nullable), value-descending, ties -> lower index; K <= 16 */
+size_t medusa_topk_rows_workspace_size(int M, int V, int K);
+int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* idx, float* val, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Whole model                                                                 */
@@ -157,6 +159,19 @@ size_t medusa_step_workspace_size(const medusa_model* m, const medusa_tree* t, i
 int medusa_step(const medusa_model* m, const medusa_tree* t, int B, int mode, float temperature, float eps,
                 float delta, medusa_state* st, int64_t L_hint, const int32_t* topk_override, void* ws,
                 size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The same step captured once into a HIP graph (all arguments, including the
+ * state and workspace pointers, are baked in); medusa_graph_launch replays it on
+ * any stream.  Capture needs a non-default stream.  Replays of one graph must not
+ * overlap each other or other work on the same state.
+ */
+typedef struct medusa_graph medusa_graph;
+int medusa_step_graph_create(const medusa_model* m, const medusa_tree* t, int B, int mode, float temperature,
+                             float eps, float delta, medusa_state* st, int64_t L_hint, const int32_t* topk_override,
+                             void* ws, size_t ws_bytes, hipStream_t stream, medusa_graph** out);
+int medusa_graph_launch(medusa_graph* g, hipStream_t stream);
+int medusa_graph_destroy(medusa_graph* g);
 
 #ifdef __cplusplus
 }

@@ -23,9 +23,11 @@ EXPORTED = [
     "medusa_tree_destroy", "medusa_heads_topk_workspace_size", "medusa_heads_topk", "tree_build_candidates",
     "tree_attention_workspace_size", "tree_attention", "evaluate_posterior_workspace_size", "evaluate_posterior",
     "kv_compact", "medusa_gemm_workspace_size", "medusa_gemm", "medusa_rmsnorm", "medusa_rope_split",
-    "medusa_embed", "medusa_gather_rows", "medusa_argmax_rows", "medusa_topk_rows",
+    "medusa_embed", "medusa_gather_rows", "medusa_argmax_rows", "medusa_topk_rows_workspace_size",
+    "medusa_topk_rows",
     "medusa_forward_workspace_size", "medusa_forward", "medusa_prefill_workspace_size", "medusa_prefill",
-    "medusa_step_workspace_size", "medusa_step",
+    "medusa_step_workspace_size", "medusa_step", "medusa_step_graph_create", "medusa_graph_launch",
+    "medusa_graph_destroy",
 ]
 
 
@@ -82,7 +84,7 @@ def _declare(lib):
         "tree_attention": (_I, [_I] * 6 + [_P, _P, _P, _L, _L, _P, _P, _P, _P, _F, _P, _P, _S, _P]),
         "evaluate_posterior_workspace_size": (_S, [_I, _I]),
         "evaluate_posterior": (_I, [_P, _I, _I, _P, _P, _I, _F, _F, _F, _P, _P, _P, _P, _P, _S, _P]),
-        "kv_compact": (_I, [_I, _P, _I, _I, _I, _I, _L] + [_P] * 10 + [_I, _P, _P, _P]),
+        "kv_compact": (_I, [_I, _P, _I, _I, _I, _I, _L] + [_P] * 9 + [_I, _P, _P, _P]),
         "medusa_gemm_workspace_size": (_S, [_I] * 5),
         "medusa_gemm": (_I, [_I] * 4 + [_P, _L, _L, _P, _L, _P, _L, _L, _I, _I, _P, _L, _L, _P, _S, _P]),
         "medusa_rmsnorm": (_I, [_I, _I, _I, _P, _P, _F, _P, _P]),
@@ -90,7 +92,8 @@ def _declare(lib):
         "medusa_embed": (_I, [_I, _I, _I, _P, _P, _I, _P, _P]),
         "medusa_gather_rows": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
         "medusa_argmax_rows": (_I, [_I, _I, _P, _L, _P, _P]),
-        "medusa_topk_rows": (_I, [_I, _I, _P, _I, _P, _P, _P]),
+        "medusa_topk_rows_workspace_size": (_S, [_I, _I, _I]),
+        "medusa_topk_rows": (_I, [_I, _I, _P, _I, _P, _P, _P, _S, _P]),
         "medusa_forward_workspace_size": (_S, [C.POINTER(ModelDesc), _I, _I, _L]),
         "medusa_forward": (_I, [C.POINTER(ModelDesc), _I, _I, _P, _P, _P, _P, _L, _L, _P, _P, _P, _P, _P, _P, _P,
                                 _S, _P]),
@@ -99,6 +102,10 @@ def _declare(lib):
         "medusa_step_workspace_size": (_S, [C.POINTER(ModelDesc), _P, _I, _L]),
         "medusa_step": (_I, [C.POINTER(ModelDesc), _P, _I, _I, _F, _F, _F, C.POINTER(StateDesc), _L, _P, _P, _S,
                              _P]),
+        "medusa_step_graph_create": (_I, [C.POINTER(ModelDesc), _P, _I, _I, _F, _F, _F, C.POINTER(StateDesc), _L,
+                                          _P, _P, _S, _P, C.POINTER(_P)]),
+        "medusa_graph_launch": (_I, [_P, _P]),
+        "medusa_graph_destroy": (_I, [_P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -195,5 +195,6 @@ def topk_rows(x, K):
     M, V = x.shape
     idx = torch.empty((M, K), dtype=torch.int32, device=x.device)
     val = torch.empty((M, K), dtype=torch.float32, device=x.device)
-    check(lib().medusa_topk_rows(M, V, ptr(x), K, ptr(idx), ptr(val), stream_ptr()))
+    ws = L._ws(None, lib().medusa_topk_rows_workspace_size(M, V, K), x.device)
+    check(lib().medusa_topk_rows(M, V, ptr(x), K, ptr(idx), ptr(val), ptr(ws), ws.numel(), stream_ptr()))
     return idx, val

@@ -7,9 +7,10 @@
 //   1. z = h + SiLU(W1 h) for all heads at once (W1 stacked [H*d, d]) with the
 //      residual fused into the product's epilogue, z stored in the input dtype;
 //   2. logits[b, k, :] = W2[k] z[b, k] as H batched products (fp32 out);
-//   3. top-K per (b, k) row: each thread keeps a sorted register list over a
-//      strided slice of the vocabulary, then K rounds of a block-wide
-//      (value desc, index asc) maximum pop the winners.
+//   3. top-K per (b, k) row in two stages: one wave per vocabulary chunk keeps
+//      a sorted per-lane register list, then K rounds of a wave-wide
+//      (value desc, index asc) maximum pop the chunk's K best; one wave per row
+//      merges the chunks' candidates the same way.
 #include "common.h"
 #include "medusa_model.h"
 
@@ -18,83 +19,109 @@ using namespace medusa;
 namespace {
 
 constexpr int TK_MAX = 16;
-constexpr int TK_THR = 256;
+constexpr int TK_PER_LANE = 8;  // vocabulary entries per lane in the first stage
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-__global__ __launch_bounds__(TK_THR) void topk_rows_kernel(int V, const float* __restrict__ x, int K,
-                                                           int32_t* __restrict__ idx, float* __restrict__ val) {
-  const int row = blockIdx.x;
-  const float* r = x + (size_t)row * V;
-  float lv[TK_MAX];
-  int li[TK_MAX];
+// Per-lane sorted list (best first) of up to TK_MAX candidates.
+struct LaneList {
+  float v[TK_MAX];
+  int i[TK_MAX];
+  __device__ __forceinline__ void init() {
 #pragma unroll
-  for (int j = 0; j < TK_MAX; ++j) {
-    lv[j] = -INFINITY;
-    li[j] = 0x7fffffff;
+    for (int j = 0; j < TK_MAX; ++j) {
+      v[j] = -INFINITY;
+      i[j] = 0x7fffffff;
+    }
   }
-  for (int k = threadIdx.x; k < V; k += TK_THR) {
-    const float v = r[k];
-    if (!better(v, k, lv[TK_MAX - 1], li[TK_MAX - 1])) continue;
-    lv[TK_MAX - 1] = v;
-    li[TK_MAX - 1] = k;
+  __device__ __forceinline__ void insert(float x, int k) {
+    if (!better(x, k, v[TK_MAX - 1], i[TK_MAX - 1])) return;
+    v[TK_MAX - 1] = x;
+    i[TK_MAX - 1] = k;
 #pragma unroll
     for (int j = TK_MAX - 1; j > 0; --j) {
-      if (better(lv[j], li[j], lv[j - 1], li[j - 1])) {
-        const float tv = lv[j];
-        lv[j] = lv[j - 1];
-        lv[j - 1] = tv;
-        const int ti = li[j];
-        li[j] = li[j - 1];
-        li[j - 1] = ti;
+      if (better(v[j], i[j], v[j - 1], i[j - 1])) {
+        const float tv = v[j];
+        v[j] = v[j - 1];
+        v[j - 1] = tv;
+        const int ti = i[j];
+        i[j] = i[j - 1];
+        i[j - 1] = ti;
       }
     }
   }
-  __shared__ float sv[TK_THR / 64];
-  __shared__ int si[TK_THR / 64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int round = 0; round < K; ++round) {
-    float bv = lv[0];
-    int bi = li[0];
+  // K rounds of a wave-wide maximum; the owning lane pops its head each round.
+  __device__ __forceinline__ void pop_k(int K, float* out_v, int* out_i) {
+    for (int r = 0; r < K; ++r) {
+      float bv = v[0];
+      int bi = i[0];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float v2 = __shfl_xor(bv, o, 64);
-      const int i2 = __shfl_xor(bi, o, 64);
-      if (better(v2, i2, bv, bi)) {
-        bv = v2;
-        bi = i2;
+      for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(bv, o, 64);
+        const int i2 = __shfl_xor(bi, o, 64);
+        if (better(v2, i2, bv, bi)) {
+          bv = v2;
+          bi = i2;
+        }
       }
-    }
-    if (lane == 0) {
-      sv[w] = bv;
-      si[w] = bi;
-    }
-    __syncthreads();
-    bv = sv[0];
-    bi = si[0];
+      if (threadIdx.x == 0) {
+        out_v[r] = bv;
+        out_i[r] = bi;
+      }
+      if (i[0] == bi && bi != 0x7fffffff) {
 #pragma unroll
-    for (int j = 1; j < TK_THR / 64; ++j)
-      if (better(sv[j], si[j], bv, bi)) {
-        bv = sv[j];
-        bi = si[j];
+        for (int j = 0; j < TK_MAX - 1; ++j) {
+          v[j] = v[j + 1];
+          i[j] = i[j + 1];
+        }
+        v[TK_MAX - 1] = -INFINITY;
+        i[TK_MAX - 1] = 0x7fffffff;
       }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      idx[(size_t)row * K + round] = bi == 0x7fffffff ? 0 : bi;
-      if (val) val[(size_t)row * K + round] = bv;
-    }
-    if (li[0] == bi && bi != 0x7fffffff) {  // the owner pops its head
-#pragma unroll
-      for (int j = 0; j < TK_MAX - 1; ++j) {
-        lv[j] = lv[j + 1];
-        li[j] = li[j + 1];
-      }
-      lv[TK_MAX - 1] = -INFINITY;
-      li[TK_MAX - 1] = 0x7fffffff;
     }
   }
+};
+
+// stage 1: grid (n_chunks, M), one wave per chunk of a row -> K candidates per chunk
+__global__ __launch_bounds__(64) void topk_stage1_kernel(int V, int chunk, const float* __restrict__ x, int K,
+                                                         float* __restrict__ cv, int* __restrict__ ci) {
+  const int ch = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
+  const float* r = x + (size_t)row * V;
+  const int k0 = ch * chunk, k1 = min(k0 + chunk, V);
+  LaneList L;
+  L.init();
+  for (int k = k0 + (int)threadIdx.x; k < k1; k += 64) L.insert(r[k], k);
+  const size_t o = ((size_t)row * nch + ch) * K;
+  L.pop_k(K, cv + o, ci + o);
+}
+
+// stage 2: grid (M), one wave merges n_chunks * K candidates
+__global__ __launch_bounds__(64) void topk_stage2_kernel(int ncand, const float* __restrict__ cv,
+                                                         const int* __restrict__ ci, int K, int32_t* __restrict__ idx,
+                                                         float* __restrict__ val) {
+  const int row = blockIdx.x;
+  LaneList L;
+  L.init();
+  for (int j = threadIdx.x; j < ncand; j += 64) L.insert(cv[(size_t)row * ncand + j], ci[(size_t)row * ncand + j]);
+  __shared__ float sv[TK_MAX];
+  __shared__ int si[TK_MAX];
+  L.pop_k(K, sv, si);
+  __syncthreads();
+  if ((int)threadIdx.x < K) {
+    const int t = si[threadIdx.x];
+    idx[(size_t)row * K + threadIdx.x] = t == 0x7fffffff ? 0 : t;
+    if (val) val[(size_t)row * K + threadIdx.x] = sv[threadIdx.x];
+  }
+}
+
+int topk_chunks(int V) {
+  int n = (V + 64 * TK_PER_LANE - 1) / (64 * TK_PER_LANE);
+  return n < 1 ? 1 : (n > 1024 ? 1024 : n);
+}
+
+size_t topk_ws(int M, int V, int K) {
+  return align_up((size_t)M * topk_chunks(V) * K * (sizeof(float) + sizeof(int)), 256);
 }
 
 struct HeadsLayout {
@@ -108,19 +135,36 @@ HeadsLayout heads_layout(int dtype, int B, int d, int V, int H) {
   L.gemm_off = L.logits_off + align_up((size_t)B * H * V * sizeof(float), 256);
   size_t g1 = medusa_gemm_workspace_size(dtype, B, H * d, d, 1);
   size_t g2 = medusa_gemm_workspace_size(dtype, B, V, d, H);
-  L.total = L.gemm_off + (g1 > g2 ? g1 : g2);
+  size_t g3 = topk_ws(B * H, V, TK_MAX);
+  size_t g = g1 > g2 ? g1 : g2;
+  L.total = L.gemm_off + (g > g3 ? g : g3);
   return L;
 }
 
 }  // namespace
 
-extern "C" int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* idx, float* val, hipStream_t stream) {
+extern "C" size_t medusa_topk_rows_workspace_size(int M, int V, int K) {
+  if (M <= 0 || V <= 0 || K <= 0) return 0;
+  return topk_ws(M, V, K);
+}
+
+extern "C" int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* idx, float* val, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
   MEDUSA_REQUIRE(M >= 0 && V > 0, MEDUSA_ERR_ARG, "topk_rows: bad sizes");
   MEDUSA_REQUIRE(K >= 1 && K <= TK_MAX && K <= V, MEDUSA_ERR_UNSUPPORTED, "topk_rows: K=%d not in [1, %d]", K, TK_MAX);
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(x && idx, MEDUSA_ERR_ARG, "topk_rows: null pointer");
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(M), dim3(TK_THR), 0, stream, V, x, K, idx, val);
-  return check_launch("topk_rows");
+  MEDUSA_REQUIRE(ws && ws_bytes >= topk_ws(M, V, K), MEDUSA_ERR_WORKSPACE, "topk_rows: workspace %zu < %zu", ws_bytes,
+                 topk_ws(M, V, K));
+  const int nch = topk_chunks(V);
+  const int chunk = (V + nch - 1) / nch;
+  float* cv = (float*)ws;
+  int* ci = (int*)((char*)ws + (size_t)M * nch * K * sizeof(float));
+  hipLaunchKernelGGL(topk_stage1_kernel, dim3(nch, M), dim3(64), 0, stream, V, chunk, x, K, cv, ci);
+  int rc = check_launch("topk_rows stage 1");
+  if (rc) return rc;
+  hipLaunchKernelGGL(topk_stage2_kernel, dim3(M), dim3(64), 0, stream, nch * K, cv, ci, K, idx, val);
+  return check_launch("topk_rows stage 2");
 }
 
 extern "C" size_t medusa_heads_topk_workspace_size(int dtype, int B, int d, int V, int H, int K) {
@@ -151,5 +195,5 @@ extern "C" int medusa_heads_topk(int dtype, int B, int d, int V, int H, int K, c
   rc = medusa_gemm(dtype, B, V, d, z, (int64_t)H * d, d, W2, (int64_t)V * d, logits, (int64_t)H * V, V, H,
                    MEDUSA_EPI_F32, nullptr, 0, 0, gws, gbytes, stream);
   if (rc) return rc;
-  return medusa_topk_rows(B * H, V, logits, K, topk_idx, topk_val, stream);
+  return medusa_topk_rows(B * H, V, logits, K, topk_idx, topk_val, gws, gbytes, stream);
 }

@@ -332,3 +332,53 @@ extern "C" int medusa_step(const medusa_model* m, const medusa_tree* t, int B, i
   return MEDUSA_OK;
 #undef CK
 }
+
+// ---------------------------------------------------------------------------
+// the step as a HIP graph: one launch replays the ~400 kernels of a step
+// ---------------------------------------------------------------------------
+struct medusa_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" int medusa_step_graph_create(const medusa_model* m, const medusa_tree* t, int B, int mode,
+                                        float temperature, float eps, float delta, medusa_state* st, int64_t L_hint,
+                                        const int32_t* topk_override, void* ws, size_t ws_bytes, hipStream_t stream,
+                                        medusa_graph** out) {
+  MEDUSA_REQUIRE(out, MEDUSA_ERR_ARG, "step_graph_create: out is null");
+  *out = nullptr;
+  MEDUSA_REQUIRE(stream != nullptr, MEDUSA_ERR_ARG, "step_graph_create: capture needs a non-default stream");
+  MEDUSA_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
+  const int rc = medusa_step(m, t, B, mode, temperature, eps, delta, st, L_hint, topk_override, ws, ws_bytes, stream);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(stream, &g);
+  if (rc) {
+    if (e == hipSuccess && g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(MEDUSA_ERR_HIP, "step_graph_create: end capture: %s", hipGetErrorString(e));
+  hipGraphExec_t ex = nullptr;
+  const hipError_t e2 = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e2 != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(MEDUSA_ERR_HIP, "step_graph_create: instantiate: %s", hipGetErrorString(e2));
+  }
+  medusa_graph* mg = new medusa_graph{g, ex};
+  *out = mg;
+  return MEDUSA_OK;
+}
+
+extern "C" int medusa_graph_launch(medusa_graph* g, hipStream_t stream) {
+  MEDUSA_REQUIRE(g, MEDUSA_ERR_ARG, "graph_launch: null graph");
+  MEDUSA_HIP(hipGraphLaunch(g->exec, stream));
+  return MEDUSA_OK;
+}
+
+extern "C" int medusa_graph_destroy(medusa_graph* g) {
+  if (!g) return MEDUSA_OK;
+  hipError_t e1 = hipGraphExecDestroy(g->exec);
+  hipError_t e2 = hipGraphDestroy(g->graph);
+  delete g;
+  if (e1 != hipSuccess || e2 != hipSuccess) return fail(MEDUSA_ERR_HIP, "graph_destroy failed");
+  return MEDUSA_OK;
+}

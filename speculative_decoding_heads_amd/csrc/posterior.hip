@@ -26,7 +26,7 @@ struct NodeStat {
   float m, Z, thr;
 };
 
-constexpr int kStatThreads = 256;
+constexpr int kStatThreads = 512;
 
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) {
@@ -46,51 +46,79 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
   __shared__ float s_f[kStatThreads / 64];
   const int lane = tid & 63, w = tid >> 6;
 
-  // argmax / max
+  // pass 1: argmax, and for typical an online sum of exp((x - running max)/tau)
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int k = tid; k < V; k += kStatThreads) {
-    const float v = x[k];
+  float z = 0.f;
+  auto visit = [&](float v, int k) {
     if (v > bv) {  // strictly greater keeps the lowest index of this thread's stripe
+      if (typical) z = z * expf((bv - v) * inv_tau) + 1.0f;
       bv = v;
       bi = k;
+    } else if (typical) {
+      z += expf((v - bv) * inv_tau);
     }
+  };
+  const bool vec = (V % 4) == 0;
+  if (vec) {
+    const float4* x4 = (const float4*)x;
+    for (int k4 = tid; k4 < V / 4; k4 += kStatThreads) {
+      const float4 f = x4[k4];
+      visit(f.x, 4 * k4);
+      visit(f.y, 4 * k4 + 1);
+      visit(f.z, 4 * k4 + 2);
+      visit(f.w, 4 * k4 + 3);
+    }
+  } else {
+    for (int k = tid; k < V; k += kStatThreads) visit(x[k], k);
   }
+  auto merge = [&](float v2, int i2, float z2) {
+    const float m = fmaxf(bv, v2);
+    if (typical && m != -INFINITY) z = z * expf((bv - m) * inv_tau) + z2 * expf((v2 - m) * inv_tau);
+    argmax_merge(bv, bi, v2, i2);
+  };
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(bv, o, 64);
     const int i2 = __shfl_xor(bi, o, 64);
-    argmax_merge(bv, bi, v2, i2);
+    const float z2 = __shfl_xor(z, o, 64);
+    merge(v2, i2, z2);
   }
   if (lane == 0) {
     s_v[w] = bv;
     s_i[w] = bi;
+    s_f[w] = z;
   }
   __syncthreads();
   bv = s_v[0];
   bi = s_i[0];
-  for (int j = 1; j < kStatThreads / 64; ++j) argmax_merge(bv, bi, s_v[j], s_i[j]);
+  z = s_f[0];
+  for (int j = 1; j < kStatThreads / 64; ++j) merge(s_v[j], s_i[j], s_f[j]);
   if (bi == 0x7fffffff) bi = 0;  // all NaN row: report token 0
   if (!typical) {
     if (tid == 0) out[(size_t)b * T + u] = NodeStat{bi, bv, 0.f, 0.f};
     return;
   }
   const float m = bv;
-  // Z = sum exp((x - m)/tau)
-  float z = 0.f;
-  for (int k = tid; k < V; k += kStatThreads) z += expf((x[k] - m) * inv_tau);
-  z = wave_sum(z);
-  __syncthreads();
-  if (lane == 0) s_f[w] = z;
-  __syncthreads();
-  float Z = 0.f;
-  for (int j = 0; j < kStatThreads / 64; ++j) Z += s_f[j];
+  const float Z = z;
   const float invZ = 1.0f / Z;
-  // H = -sum q log(q + 1e-5)
+  // pass 2: H = -sum q log(q + 1e-5)
   float hsum = 0.f;
-  for (int k = tid; k < V; k += kStatThreads) {
-    const float q = expf((x[k] - m) * inv_tau) * invZ;
+  auto hterm = [&](float v) {
+    const float q = expf((v - m) * inv_tau) * invZ;
     hsum += q * logf(q + 1e-5f);
+  };
+  if (vec) {
+    const float4* x4 = (const float4*)x;
+    for (int k4 = tid; k4 < V / 4; k4 += kStatThreads) {
+      const float4 f = x4[k4];
+      hterm(f.x);
+      hterm(f.y);
+      hterm(f.z);
+      hterm(f.w);
+    }
+  } else {
+    for (int k = tid; k < V; k += kStatThreads) hterm(x[k]);
   }
   hsum = wave_sum(hsum);
   __syncthreads();

@@ -127,6 +127,42 @@ def step_workspace_size(model, tree, B, L_hint):
     return lib().medusa_step_workspace_size(C.byref(model.desc), tree.handle, B, int(L_hint))
 
 
+class StepGraph:
+    """One verify step captured into a HIP graph (medusa_step_graph_create); replay() launches it.
+
+    Capture happens on ``stream`` (a non-default torch stream); every pointer,
+    including the state and workspace, is baked into the graph, so keep them alive."""
+
+    def __init__(self, model, tree, state, mode, temperature=0.0, eps=0.09, delta=0.3, L_hint=None, ws=None,
+                 stream=None):
+        torch = _torch()
+        L_hint = state.Lmax if L_hint is None else int(L_hint)
+        self.ws = L._ws(ws, step_workspace_size(model, tree, state.B, L_hint), state.Kc.device)
+        self.stream = stream or torch.cuda.Stream()
+        self.refs = (model, tree, state)
+        h = C.c_void_p()
+        torch.cuda.synchronize()
+        check(lib().medusa_step_graph_create(C.byref(model.desc), tree.handle, state.B, int(mode), float(temperature),
+                                             float(eps), float(delta), C.byref(state.desc), L_hint, None,
+                                             ptr(self.ws), self.ws.numel(), self.stream.cuda_stream, C.byref(h)))
+        self._h = h
+
+    def replay(self, stream=None):
+        s = stream if stream is not None else _torch().cuda.current_stream()
+        check(lib().medusa_graph_launch(self._h, s.cuda_stream))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            check(lib().medusa_graph_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def step(model, tree, state, mode, temperature=0.0, eps=0.09, delta=0.3, L_hint=None, topk_override=None, ws=None):
     B = state.B
     L_hint = state.Lmax if L_hint is None else int(L_hint)

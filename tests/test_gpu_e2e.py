@@ -212,3 +212,33 @@ def test_bf16_step_acceptance_on_identical_logits(dev, mode):
         assert torch.equal(st.Vc[:, b, :, s0:s0 + a + 1], Vt[:, b][:, :, rows])
         assert int(to_np(st.seq_len)[b]) == s0 + a + 1
         assert torch.equal(st.h_sel[b], h[b, int(to_np(st.sel_node)[b])])
+
+
+def test_step_graph_replays_match_eager(dev):
+    """The captured step, replayed several times with eager work and synchronisations in
+    between, gives bit-identical state to the eager step run from the same start."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd.model import Model, State, StepGraph, prefill, step
+    say("e2e step graph vs eager")
+    (params, heads), Cfg = _small_bf16_model(7)
+    P, H = _upload(params, heads, torch.bfloat16, dev)
+    model = Model(P, H, max_pos=1024)
+    tree = api.Tree(PAGE_TREE_CHOICES)
+    B, Lmax = 2, 256
+    prompt = torch.from_numpy(prompt_tokens(3, B, 40, Cfg.vocab).astype(np.int32)).to(dev)
+    eager, graphed = State(model, B, Lmax, 64), State(model, B, Lmax, 64)
+    prefill(model, eager, prompt)
+    prefill(model, graphed, prompt)
+    torch.cuda.synchronize()
+    g = StepGraph(model, tree, graphed, TYPICAL, 0.7, 0.09, 0.3, L_hint=Lmax)
+    for r in range(4):
+        step(model, tree, eager, TYPICAL, 0.7, 0.09, 0.3, L_hint=Lmax)
+        with torch.cuda.stream(g.stream):
+            g.replay(g.stream)
+        g.stream.synchronize()
+        torch.cuda.synchronize()
+        _ = (eager.Kc.float().sum() + 1).item()  # unrelated eager work between replays
+        for name in ("seq_len", "root", "n_out", "out_tokens", "best", "accept_len", "sel_node", "h_sel", "Kc", "Vc"):
+            assert torch.equal(getattr(eager, name), getattr(graphed, name)), (r, name)
+    g.close()
