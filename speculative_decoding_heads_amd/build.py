@@ -20,6 +20,9 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     # keep hipcc from forming packed fp32 ops on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: with AGPR accumulators the register
+    # allocator rotates them through v_accvgpr moves on every loop iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
     "-I" + INCLUDE, "-I" + CSRC,
 ]

@@ -7,13 +7,14 @@
 // Both are weight-streaming products with few rows (M = batch or batch*T), so
 // the bf16 kernel is built for HBM streaming, not for square tiles:
 //
-//  * bf16: a workgroup (4 waves) owns 64 rows of W and up to 64 rows of A over a
-//    K range; W is the MFMA A-operand (16x16x32 bf16, fp32 accumulate) so each
-//    lane loads 16 contiguous bytes of one W row per k-step, and the four waves
-//    take interleaved k-steps of the range and are summed through LDS in a fixed
-//    order.  When N/64 is too small to fill the chip, the K range is split
-//    across workgroups and a second kernel adds the fp32 partials in a fixed
-//    order and applies the epilogue.
+//  * bf16: a wave owns 32 (M > 32) or 64 rows of W and up to 64 rows of A; W is
+//    the MFMA A-operand (16x16x32 bf16, fp32 accumulate) so each lane loads 16
+//    contiguous bytes of one W row per k-step.  The four waves of a workgroup
+//    take neighbouring W rows over the same k range (their A loads coincide and
+//    hit in L1), each with a two-stage register pipeline.  When the grid would
+//    be too small to keep ~8 waves per CU busy the K range is also split across
+//    workgroups; a second kernel then adds the fp32 partials in a fixed order
+//    and applies the epilogue.
 //  * fp32: one thread per output with a sequential k loop, so a row's result
 //    does not depend on M or on the row's position (plain decode and tree
 //    verification agree bit for bit).
@@ -21,6 +22,8 @@
 // Epilogues: store fp32; store in dtype; residual add; Medusa residual
 // (A[m, n mod K] + SiLU(acc), the head's h + SiLU(W1 h) with W1 of size K x K);
 // SwiGLU on row-interleaved gate/up weights (row 2j = gate j, row 2j+1 = up j).
+#include <stdlib.h>
+
 #include "common.h"
 #include "medusa_model.h"
 
@@ -114,125 +117,26 @@ __global__ __launch_bounds__(256) void gemm_valu_kernel(int M, int N, int K, con
 // ---------------------------------------------------------------------------
 // bf16 MFMA streaming kernel
 // ---------------------------------------------------------------------------
-constexpr int GN = 64;   // W rows per workgroup
-constexpr int GM = 64;   // A rows per workgroup (max)
-constexpr int GK = 32;   // k per MFMA step
-constexpr int GTHR = 256;
+constexpr int GK = 32;     // k per MFMA step (16x16x32 bf16)
+constexpr int GTHR = 256;  // 4 waves
+constexpr int GM = 64;     // A rows per tile (max)
 
 union F8 {
   uint4 u;
   bf16x8 v;
 };
 
-// grid (N/64, ceil(M/64) * SK, batch).  MB = number of 16-row blocks of A used.
-template <int MB>
-__global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, const bf16_t* __restrict__ A, int64_t lda,
-                                                         int64_t sA, const bf16_t* __restrict__ W, int64_t sW,
-                                                         int SK, int ksteps_per_split, EpiArgs e, int64_t sC,
-                                                         int64_t sR, float* __restrict__ part) {
-  __shared__ float red[2][GN * GM];  // wave partial sums
-  const int bz = blockIdx.z;
-  const int nt = blockIdx.x;
-  const int mt = blockIdx.y / SK;
-  const int ks = blockIdx.y % SK;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, lg = lane >> 4;
-  A += bz * sA;
-  W += bz * sW;
-  const int n0 = nt * GN, m0 = mt * GM;
-  const int nsteps = K / GK;
-  const int s_begin = ks * ksteps_per_split;
-  const int s_end = min(s_begin + ksteps_per_split, nsteps);
-
-  f32x4 acc[4][MB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // rows this lane feeds
-  const bf16_t* wrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int n = n0 + i * 16 + l16;
-    if (n >= N) n = N - 1;  // clamp (result discarded)
-    wrow[i] = W + (size_t)n * K + lg * 8;
-  }
-  const bf16_t* arow[MB];
-  bool avalid[MB];
-#pragma unroll
-  for (int j = 0; j < MB; ++j) {
-    const int m = m0 + j * 16 + l16;
-    avalid[j] = m < M;
-    arow[j] = A + (size_t)(avalid[j] ? m : 0) * lda + lg * 8;
-  }
-
-  constexpr int U = 4;  // k-steps in flight per wave
-  int s = s_begin + w;
-  for (; s + (U - 1) * 4 < s_end; s += U * 4) {
-    F8 wf[U][4], af[U][MB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (s + u * 4) * GK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wf[u][i].u = *(const uint4*)(wrow[i] + k);
-#pragma unroll
-      for (int j = 0; j < MB; ++j) af[u][j].u = avalid[j] ? *(const uint4*)(arow[j] + k) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < MB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[u][i].v, af[u][j].v, acc[i][j], 0, 0, 0);
-  }
-  for (; s < s_end; s += 4) {
-    const int k = s * GK;
-    F8 wf[4], af[MB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wf[i].u = *(const uint4*)(wrow[i] + k);
-#pragma unroll
-    for (int j = 0; j < MB; ++j) af[j].u = avalid[j] ? *(const uint4*)(arow[j] + k) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < MB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i].v, af[j].v, acc[i][j], 0, 0, 0);
-  }
-
-  // fixed-order reduction of the 4 waves: (w2 -> w0, w3 -> w1), then (w1 -> w0)
-  // C layout: acc[i][j][r] is W row n0 + 16i + 4*lg + r, A row m0 + 16j + l16.
-  auto put = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < MB; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[slot][(i * 16 + 4 * lg + r) * GM + j * 16 + l16] = acc[i][j][r];
-  };
-  auto add = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < MB; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] += red[slot][(i * 16 + 4 * lg + r) * GM + j * 16 + l16];
-  };
-  if (w >= 2) put(w - 2);
-  __syncthreads();
-  if (w < 2) add(w);
-  __syncthreads();
-  if (w == 1) put(0);
-  __syncthreads();
-  if (w != 0) return;
-  add(0);
-
+// Write a wave's (NR*16) x (MB*16) accumulator tile: fp32 partials when the
+// K range is split (layout [batch][SK][M][N]), else the epilogue.  C layout of
+// the 16x16 MFMA: acc[i][j][r] is W row n0 + 16i + 4*lg + r, A row m0 + 16j + l16.
+template <int NR, int MB>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[NR][MB], int n0, int m0, int M, int N, int SK, int ks,
+                                           int bz, const EpiArgs& e, int64_t sC, int64_t sR, const bf16_t* A,
+                                           float* __restrict__ part, int l16, int lg) {
   if (SK > 1) {
-    // partials [batch][SK][M][N]
     float* pp = part + (((size_t)bz * SK + ks) * M) * N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NR; ++i)
 #pragma unroll
       for (int j = 0; j < MB; ++j) {
         const int m = m0 + j * 16 + l16;
@@ -250,7 +154,7 @@ __global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, co
   if (e.R) eb.R = (const char*)e.R + bz * sR * 2;
   eb.A = A;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NR; ++i)
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
       const int m = m0 + j * 16 + l16;
@@ -265,6 +169,289 @@ __global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, co
           if (nb + r < N) epi_store<bf16_t>(eb, m, nb + r, acc[i][j][r]);
       }
     }
+}
+
+// Each wave owns an (NR*16 W rows) x (MB*16 A rows) output tile.  With KW the
+// four waves of a workgroup cover consecutive k ranges of the same tile and are
+// summed through LDS in wave order; without it they own four neighbouring W
+// tiles over the same k range (their A loads coincide and hit in L1).  Loads run
+// two pipeline stages of U k-steps ahead: the next stage is issued before the
+// current one is multiplied.  When the grid is split along K (SK > 1) the fp32
+// partials are summed by splitk_reduce_kernel.
+// grid (N tiles of (KW ? 1 : 4)*NR*16 rows, m tiles * SK, batch).
+template <int MB, int NR, int U, bool KW>
+__global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, const bf16_t* __restrict__ A, int64_t lda,
+                                                         int64_t sA, const bf16_t* __restrict__ W, int64_t sW,
+                                                         int SK, EpiArgs e, int64_t sC, int64_t sR,
+                                                         float* __restrict__ part) {
+  constexpr int TN = NR * 16, TM = MB * 16;
+  __shared__ float red[KW ? 3 : 1][KW ? TN * TM : 1];
+  const int bz = blockIdx.z;
+  const int nt = blockIdx.x;
+  const int mt = blockIdx.y / SK;
+  const int ks = blockIdx.y % SK;
+  // the wave index is uniform: keep it (and the k range below) in scalar registers
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  A += bz * sA;
+  W += bz * sW;
+  const int n0 = (KW ? nt : nt * 4 + w) * TN, m0 = mt * GM;
+  const int nchunks = (K / GK) / U;
+  const int parts = KW ? SK * 4 : SK, pi = KW ? ks * 4 + w : ks;
+  const int c0 = (int)((int64_t)nchunks * pi / parts), c1 = (int)((int64_t)nchunks * (pi + 1) / parts);
+
+  // rows past N / M are clamped to the last row; their results are discarded
+  const bf16_t* wrow[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int n = min(n0 + i * 16 + l16, N - 1);
+    wrow[i] = W + (size_t)n * K + lg * 8;
+  }
+  const bf16_t* arow[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const int m = min(m0 + j * 16 + l16, M - 1);
+    arow[j] = A + (size_t)m * lda + lg * 8;
+  }
+  f32x4 acc[NR][MB];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  struct Stage {
+    F8 w[U][NR];
+    F8 a[U][MB];
+  };
+  Stage S0, S1;
+  auto load = [&](Stage& s, int c) {
+    const int k = c * U * GK;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) s.w[u][i].u = *(const uint4*)(wrow[i] + k + u * GK);
+#pragma unroll
+      for (int j = 0; j < MB; ++j) s.a[u][j].u = *(const uint4*)(arow[j] + k + u * GK);
+    }
+  };
+  auto comp = [&](const Stage& s) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(s.w[u][i].v, s.a[u][j].v, acc[i][j], 0, 0, 0);
+  };
+  // Loads past the wave's last chunk are clamped to that chunk (cache hits, never
+  // multiplied) so the loop body has no branches around its loads.
+  if (c0 < c1) {
+    load(S0, c0);
+    load(S1, min(c0 + 1, c1 - 1));
+    int c = c0;
+    // sched_barrier keeps the compiler from sinking a stage's loads below the
+    // next stage's multiplies (which would serialise load latency)
+    for (; c + 1 < c1; c += 2) {
+      comp(S0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(S0, min(c + 2, c1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      comp(S1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(S1, min(c + 3, c1 - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c < c1) comp(S0);
+  }
+
+  // C layout: acc[i][j][r] is W row n0 + 16i + 4*lg + r, A row m0 + 16j + l16
+  if (KW) {
+    if (w > 0) {
+      float* dst = red[w - 1];
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(i * 16 + 4 * lg + r) * TM + j * 16 + l16] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] += red[q][(i * 16 + 4 * lg + r) * TM + j * 16 + l16];
+  }
+  store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
+}
+
+// Kernel for M > 32.  The four waves of a workgroup form KG k-groups of 4/KG
+// waves; the waves of a k-group own neighbouring (NR*16)-row W tiles and walk
+// the same k range, and each k-group stages the 64 A rows of its current chunk
+// (U k-steps) once in LDS, so A costs one global read per k-group instead of
+// one per wave (re-reading A per wave caps these products at about half the
+// HBM rate).  W fragments go straight from global memory to registers, NS
+// chunks ahead; A goes global -> registers -> LDS one chunk ahead through two
+// LDS buffers per k-group, with one barrier per chunk.  Staged rows are padded
+// by 16 bytes so the 16 rows that one ds_read_b128 touches fall in distinct
+// banks.  The k-groups are summed through LDS in group order at the end; a
+// K split across workgroups (SK > 1) leaves fp32 partials for
+// splitk_reduce_kernel.  grid (N tiles of (4/KG)*NR*16 rows, m tiles * SK, batch).
+template <int NR, int U, int NS, int KG>
+__global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, const bf16_t* __restrict__ A, int64_t lda,
+                                                        int64_t sA, const bf16_t* __restrict__ W, int64_t sW, int SK,
+                                                        EpiArgs e, int64_t sC, int64_t sR, float* __restrict__ part) {
+  constexpr int MB = 4, TN = NR * 16, TM = MB * 16;
+  constexpr int NG = 4 / KG;               // waves per k-group
+  constexpr int ROWB = U * GK * 2 + 16;    // bytes per staged A row
+  constexpr int PPR = U * GK * 2 / 16;     // 16-byte pieces per A row and chunk
+  constexpr int PPT = GM * PPR / (NG * 64);  // pieces per thread and chunk
+  constexpr int BUFB = GM * ROWB;
+  constexpr int A_BYTES = KG * 2 * BUFB;
+  constexpr int R_BYTES = KG > 1 ? (KG - 1) * NG * TN * TM * 4 : 0;
+  __shared__ __align__(16) char lds[A_BYTES > R_BYTES ? A_BYTES : R_BYTES];
+  const int bz = blockIdx.z;
+  const int nt = blockIdx.x;
+  const int mt = blockIdx.y / SK;
+  const int ks = blockIdx.y % SK;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int kg = w / NG, ng = w % NG, gtid = tid - kg * NG * 64;
+  A += bz * sA;
+  W += bz * sW;
+  const int n0 = (nt * NG + ng) * TN, m0 = mt * GM;
+  const int nchunks = (K / GK) / U;
+  const int c0 = (int)((int64_t)nchunks * ks / SK), c1 = (int)((int64_t)nchunks * (ks + 1) / SK);
+  // every k-group runs `per` pipeline steps (uniform over the workgroup, so
+  // all waves meet the same barriers); its real chunks are [g0, g1)
+  const int per = (c1 - c0 + KG - 1) / KG;
+  const int g0 = c0 + kg * per, g1 = min(g0 + per, c1);
+  auto clampc = [&](int v) { return max(min(g0 + v, g1 - 1), 0); };
+  char* albase = lds + kg * 2 * BUFB;
+
+  const bf16_t* wrow[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) wrow[i] = W + (size_t)min(n0 + i * 16 + l16, N - 1) * K + lg * 8;
+  // a k-group's NG*64 threads stage GM * PPR pieces: thread gtid takes gtid + NG*64*q
+  const bf16_t* apiece[PPT];
+  int aoff[PPT];
+#pragma unroll
+  for (int q = 0; q < PPT; ++q) {
+    const int pc = gtid + NG * 64 * q, r = pc / PPR, cp = pc % PPR;
+    apiece[q] = A + (size_t)min(m0 + r, M - 1) * lda + cp * 8;
+    aoff[q] = r * ROWB + cp * 16;
+  }
+  f32x4 acc[NR][MB];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // A pieces travel as native vectors (a uint4 struct copy would become a
+  // memcpy through private memory)
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  struct Stage {
+    F8 w[U][NR];
+    u32x4 a[PPT];
+  };
+  Stage S[NS];
+  // A pieces are issued before W so waiting for them does not wait for W
+  auto gload = [&](Stage& st, int c) {
+    const int k = c * U * GK;
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) st.a[q] = *(const u32x4*)(apiece[q] + k);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < NR; ++i) st.w[u][i].u = *(const uint4*)(wrow[i] + k + u * GK);
+  };
+  auto stage = [&](int buf, const Stage& st) {
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) *(u32x4*)(albase + buf * BUFB + aoff[q]) = st.a[q];
+  };
+  auto comp = [&](int buf, const Stage& st) {
+    const char* base = albase + buf * BUFB;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      F8 b[MB];
+#pragma unroll
+      for (int j = 0; j < MB; ++j) b[j].u = *(const uint4*)(base + (j * 16 + l16) * ROWB + u * GK * 2 + lg * 16);
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.w[u][i].v, b[j].v, acc[i][j], 0, 0, 0);
+    }
+  };
+  // Step v of a k-group handles chunk g0 + v from register stage v % NS and
+  // LDS buffer v % 2 (NS is even).  Steps past the group's last chunk load a
+  // clamped, valid chunk and skip the multiply.  An LDS buffer is rewritten
+  // only after the barrier that follows every wave's last read of it.
+  // sched_barrier keeps each phase in program order: the scheduler would
+  // otherwise move W loads ahead of A loads, and the in-order load counter
+  // would then make the LDS store wait for W as well.
+  static_assert(NS % 2 == 0, "stage count must be even");
+  if (per > 0) {
+#pragma unroll
+    for (int t = 0; t < NS; ++t) gload(S[t], clampc(t));
+    stage(0, S[0]);
+    __syncthreads();
+    int v = 0;
+    for (; v + NS <= per; v += NS) {
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        if (g0 + v + t < g1) comp(t & 1, S[t]);
+        __builtin_amdgcn_sched_barrier(0);
+        gload(S[t], clampc(v + t + NS));
+        __builtin_amdgcn_sched_barrier(0);
+        stage((t + 1) & 1, S[(t + 1) % NS]);
+        __syncthreads();
+      }
+    }
+    // 0 <= per - v < NS steps left, in stages 0.. with step v staged in buffer 0
+    const int left = per - v;
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) {
+      if (t < left) {
+        if (g0 + v + t < g1) comp(t & 1, S[t]);
+        if (t + 1 < left) {
+          stage((t + 1) & 1, S[t + 1]);
+          __syncthreads();
+        }
+      }
+    }
+  }
+  if (KG > 1) {
+    // sum the k-groups in group order through LDS (the A buffers are free now)
+    float* red = (float*)lds;
+    __syncthreads();
+    if (kg > 0) {
+      float* dst = red + ((kg - 1) * NG + ng) * TN * TM;
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(i * 16 + 4 * lg + r) * TM + j * 16 + l16] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int q = 1; q < KG; ++q) {
+      const float* src = red + ((q - 1) * NG + ng) * TN * TM;
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] += src[(i * 16 + 4 * lg + r) * TM + j * 16 + l16];
+    }
+  }
+  store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
 }
 
 // Sum split-K partials in split order and apply the epilogue.
@@ -296,24 +483,72 @@ __global__ void splitk_reduce_kernel(int M, int N, int SK, const float* __restri
 }
 
 struct GemmPlan {
-  int SK, ksteps_per_split, m_tiles;
+  int SK, MB, NR, U, m_tiles, n_tiles;
+  bool KW;   // register kernel: the four waves split K
+  bool LDS;  // M > 32: A staged in LDS (gemm_lds_kernel)
+  int NS;    // register stages of gemm_lds_kernel
+  int KG;    // k-groups per workgroup of gemm_lds_kernel
   size_t part_bytes;
 };
 
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return s ? atoi(s) : dflt;
+}
+
+// Tile shape, pipeline depth and K split for one product.  The MEDUSA_GEMM_*
+// environment variables override the defaults for tuning runs only.
 GemmPlan gemm_plan(int M, int N, int K, int batch) {
+  static const int e_nr4 = env_int("MEDUSA_GEMM_NR4", 0);   // register kernel: 64 W rows per wave at M > 32
+  static const int e_kw = env_int("MEDUSA_GEMM_KW", 1);     // register kernel: waves split K
+  static const int e_lds = env_int("MEDUSA_GEMM_LDS", 1);   // M > 32 on gemm_lds_kernel
+  static const int e_lnr = env_int("MEDUSA_GEMM_LNR", 0);   // gemm_lds_kernel: W row blocks per wave (1 | 2)
+  static const int e_kg = env_int("MEDUSA_GEMM_KG", 1);     // gemm_lds_kernel: k-groups (1 | 2 | 4)
+  static const int e_ns = env_int("MEDUSA_GEMM_NS", 4);     // gemm_lds_kernel: register stages (2 | 4)
+  static const int e_u = env_int("MEDUSA_GEMM_U", 2);       // k-steps per chunk cap (1 | 2 | 4)
+  static const int e_waves = env_int("MEDUSA_GEMM_WAVES", 1024);
+  static const int e_sk = env_int("MEDUSA_GEMM_SK", 0);     // forced K split (0: from the wave target)
   GemmPlan p;
+  const int mrows = M < GM ? M : GM;
+  p.MB = mrows <= 16 ? 1 : (mrows <= 32 ? 2 : 4);
   p.m_tiles = (M + GM - 1) / GM;
-  const int n_tiles = (N + GN - 1) / GN;
+  p.LDS = p.MB == 4 && e_lds;
+  p.KW = e_kw && !p.LDS;
+  p.NS = e_ns == 2 ? 2 : 4;
+  p.KG = p.LDS ? (e_kg == 4 ? 4 : (e_kg == 2 ? 2 : 1)) : 1;
   const int nsteps = K / GK;
-  const int64_t wgs = (int64_t)n_tiles * p.m_tiles * batch;
-  // fill ~512 workgroups; each split keeps >= 16 k-steps (4 per wave)
-  int sk = (int)((512 + wgs - 1) / wgs);
-  const int skmax = nsteps / 16 > 0 ? nsteps / 16 : 1;
-  if (sk > skmax) sk = skmax;
-  if (sk < 1) sk = 1;
-  p.ksteps_per_split = (nsteps + sk - 1) / sk;
-  p.ksteps_per_split = (p.ksteps_per_split + 3) / 4 * 4;  // whole wave rounds
-  p.SK = (nsteps + p.ksteps_per_split - 1) / p.ksteps_per_split;
+  p.U = nsteps % 4 == 0 ? 4 : (nsteps % 2 == 0 ? 2 : 1);
+  while (p.U > e_u && p.U > 1) p.U /= 2;
+  if (p.LDS) {
+    if (p.U > 2) p.U = 2;
+    if (p.KG == 4) p.U = 1;
+    // One workgroup per CU streams best (a second one on some CUs leaves the
+    // rest idle at the end): take 128-row tiles when they give >= 160
+    // workgroups, else 64-row tiles, and split K across workgroups only when
+    // even those leave most CUs idle.
+    const int64_t per_tile = (int64_t)p.m_tiles * batch;
+    const int64_t wg2 = (N + 127) / 128 * per_tile, wg1 = (N + 63) / 64 * per_tile;
+    p.NR = e_lnr == 1 || e_lnr == 2 ? e_lnr : (wg2 >= 160 ? 2 : 1);
+    const int wg_rows = (4 / p.KG) * p.NR * 16;
+    p.n_tiles = (N + wg_rows - 1) / wg_rows;
+    const int64_t wgs = (int64_t)p.n_tiles * per_tile;
+    int sk = e_sk > 0 ? e_sk : (wgs >= 160 ? 1 : (int)(256 / wgs));
+    (void)wg1;
+    const int nchunks = nsteps / p.U;
+    const int skmax = nchunks / (4 * p.KG) > 0 ? nchunks / (4 * p.KG) : 1;
+    p.SK = sk < 1 ? 1 : (sk > skmax ? skmax : sk);
+  } else {
+    p.NR = p.MB == 4 && !e_nr4 ? 2 : 4;
+    const int wg_rows = (p.KW ? 1 : 4) * p.NR * 16;
+    p.n_tiles = (N + wg_rows - 1) / wg_rows;
+    const int nchunks = nsteps / p.U;
+    const int64_t waves = (int64_t)p.n_tiles * p.m_tiles * batch * 4;
+    // aim at ~8 waves per CU while each wave keeps >= 2 chunks
+    int sk = e_sk > 0 ? e_sk : (int)((e_waves + waves - 1) / waves);
+    const int per_wg = p.KW ? 4 : 1;
+    const int skmax = nchunks / (2 * per_wg) > 0 ? nchunks / (2 * per_wg) : 1;
+    p.SK = sk < 1 ? 1 : (sk > skmax ? skmax : sk);
+  }
   p.part_bytes = p.SK > 1 ? align_up((size_t)batch * p.SK * M * N * sizeof(float), 256) : 0;
   return p;
 }
@@ -353,16 +588,59 @@ extern "C" int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_
   GemmPlan p = gemm_plan(M, N, K, batch);
   MEDUSA_REQUIRE(ws_bytes >= p.part_bytes && (p.SK == 1 || ws), MEDUSA_ERR_WORKSPACE, "gemm: workspace %zu < %zu",
                  ws_bytes, p.part_bytes);
-  dim3 grid((N + GN - 1) / GN, p.m_tiles * p.SK, batch);
-  const int mrows = M < GM ? M : GM;
-  const int MB = (mrows + 15) / 16;
-#define GEMM_LAUNCH(MBV)                                                                                          \
-  hipLaunchKernelGGL(gemm_bf16_kernel<MBV>, grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, lda, strideA, \
-                     (const bf16_t*)W, strideW, p.SK, p.ksteps_per_split, e, strideC, strideR, (float*)ws)
-  if (MB <= 1) GEMM_LAUNCH(1);
-  else if (MB == 2) GEMM_LAUNCH(2);
-  else GEMM_LAUNCH(4);
+  dim3 grid(p.n_tiles, p.m_tiles * p.SK, batch);
+#define GEMM_LAUNCH_KW(MBV, NRV, UV, KWV)                                                                      \
+  hipLaunchKernelGGL((gemm_bf16_kernel<MBV, NRV, UV, KWV>), grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, \
+                     lda, strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
+#define GEMM_LAUNCH(MBV, NRV, UV)              \
+  do {                                         \
+    if (p.KW) GEMM_LAUNCH_KW(MBV, NRV, UV, true); \
+    else GEMM_LAUNCH_KW(MBV, NRV, UV, false);     \
+  } while (0)
+#define GEMM_LAUNCH_LDS_G(NRV, UV, NSV, KGV)                                                                 \
+  hipLaunchKernelGGL((gemm_lds_kernel<NRV, UV, NSV, KGV>), grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, \
+                     lda, strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
+#define GEMM_LAUNCH_LDS_U(NRV, NSV, KGV)                 \
+  do {                                                   \
+    if (p.U == 2 && KGV < 4) GEMM_LAUNCH_LDS_G(NRV, (KGV < 4 ? 2 : 1), NSV, KGV); \
+    else GEMM_LAUNCH_LDS_G(NRV, 1, NSV, KGV);            \
+  } while (0)
+#define GEMM_LAUNCH_LDS_K(NRV, NSV)                                   \
+  do {                                                                \
+    if (p.KG == 4) GEMM_LAUNCH_LDS_U(NRV, NSV, 4);                    \
+    else if (p.KG == 2) GEMM_LAUNCH_LDS_U(NRV, NSV, 2);               \
+    else GEMM_LAUNCH_LDS_U(NRV, NSV, 1);                              \
+  } while (0)
+  if (p.LDS) {
+    if (p.NR == 1) {
+      if (p.NS == 4) GEMM_LAUNCH_LDS_K(1, 4);
+      else GEMM_LAUNCH_LDS_K(1, 2);
+    } else {
+      if (p.NS == 4) GEMM_LAUNCH_LDS_K(2, 4);
+      else GEMM_LAUNCH_LDS_K(2, 2);
+    }
+  } else if (p.MB == 1) {
+    if (p.U == 4) GEMM_LAUNCH(1, 4, 4);
+    else if (p.U == 2) GEMM_LAUNCH(1, 4, 2);
+    else GEMM_LAUNCH(1, 4, 1);
+  } else if (p.MB == 2) {
+    if (p.U == 4) GEMM_LAUNCH(2, 4, 4);
+    else if (p.U == 2) GEMM_LAUNCH(2, 4, 2);
+    else GEMM_LAUNCH(2, 4, 1);
+  } else if (p.NR == 2) {
+    if (p.U == 4) GEMM_LAUNCH(4, 2, 4);
+    else if (p.U == 2) GEMM_LAUNCH(4, 2, 2);
+    else GEMM_LAUNCH(4, 2, 1);
+  } else {
+    if (p.U == 4) GEMM_LAUNCH(4, 4, 4);
+    else if (p.U == 2) GEMM_LAUNCH(4, 4, 2);
+    else GEMM_LAUNCH(4, 4, 1);
+  }
 #undef GEMM_LAUNCH
+#undef GEMM_LAUNCH_KW
+#undef GEMM_LAUNCH_LDS_G
+#undef GEMM_LAUNCH_LDS_U
+#undef GEMM_LAUNCH_LDS_K
   int rc = check_launch("gemm bf16");
   if (rc) return rc;
   if (p.SK > 1) {
