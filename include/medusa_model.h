@@ -47,6 +47,21 @@ int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_t lda, int6
 int medusa_rmsnorm(int dtype, int M, int N, const void* x, const void* w, float eps, void* y, hipStream_t stream);
 
 /*
+ * Residual projection followed by the next pre-norm (the decoder block's
+ * "h = h + attn(.) W_o" / "h = h + mlp(.) W_down" and the RMSNorm that feeds the
+ * next sub-layer), in one call:
+ *   X[m,:] = X[m,:] + A[m,:] W^T        X [M, N] in dtype, updated in place
+ *   Y[m,:] = X[m,:] / sqrt(mean(X[m,:]^2) + eps) * norm_w      (over the stored X)
+ * A [M, K] with leading dimension lda, W [N, K].  bf16 needs K % 32 == 0,
+ * N % 8 == 0, N <= 8192 and 16-byte aligned rows; the product's fp32 partials
+ * go to the workspace and one kernel adds them, stores X and normalises.
+ * fp32 runs the plain product and RMSNorm kernels.
+ */
+size_t medusa_gemm_resid_rmsnorm_workspace_size(int dtype, int M, int N, int K);
+int medusa_gemm_resid_rmsnorm(int dtype, int M, int N, int K, const void* A, int64_t lda, const void* W, void* X,
+                              const void* norm_w, float eps, void* Y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Split a fused fp32 Q/K/V projection [B*T, (Hq + 2*Hkv)*Dh] into
  *   q  [B, T, Hq, Dh] (dtype) rotated at pos,   Kt [B, Hkv, T, Dh] rotated,   Vt [B, Hkv, T, Dh]
  * Rotary embedding, rotate-half: x'[i] = x[i] cos - x[i+Dh/2] sin, x'[i+Dh/2] = x[i+Dh/2] cos + x[i] sin,

@@ -22,7 +22,8 @@ EXPORTED = [
     "medusa_tree_anc_device",
     "medusa_tree_destroy", "medusa_heads_topk_workspace_size", "medusa_heads_topk", "tree_build_candidates",
     "tree_attention_workspace_size", "tree_attention", "evaluate_posterior_workspace_size", "evaluate_posterior",
-    "kv_compact", "medusa_gemm_workspace_size", "medusa_gemm", "medusa_rmsnorm", "medusa_rope_split",
+    "kv_compact", "medusa_gemm_workspace_size", "medusa_gemm", "medusa_rmsnorm",
+    "medusa_gemm_resid_rmsnorm_workspace_size", "medusa_gemm_resid_rmsnorm", "medusa_rope_split",
     "medusa_embed", "medusa_gather_rows", "medusa_argmax_rows", "medusa_topk_rows_workspace_size",
     "medusa_topk_rows",
     "medusa_forward_workspace_size", "medusa_forward", "medusa_prefill_workspace_size", "medusa_prefill",
@@ -88,6 +89,8 @@ def _declare(lib):
         "medusa_gemm_workspace_size": (_S, [_I] * 5),
         "medusa_gemm": (_I, [_I] * 4 + [_P, _L, _L, _P, _L, _P, _L, _L, _I, _I, _P, _L, _L, _P, _S, _P]),
         "medusa_rmsnorm": (_I, [_I, _I, _I, _P, _P, _F, _P, _P]),
+        "medusa_gemm_resid_rmsnorm_workspace_size": (_S, [_I] * 4),
+        "medusa_gemm_resid_rmsnorm": (_I, [_I] * 4 + [_P, _L, _P, _P, _P, _F, _P, _P, _S, _P]),
         "medusa_rope_split": (_I, [_I] * 6 + [_P] * 4 + [_I, _P, _P, _P, _P]),
         "medusa_embed": (_I, [_I, _I, _I, _P, _P, _I, _P, _P]),
         "medusa_gather_rows": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),

@@ -182,6 +182,18 @@ def rmsnorm(x, w, eps, out=None):
     return out
 
 
+def gemm_resid_rmsnorm(A, W, X, norm_w, eps, Y=None, ws=None):
+    """X += A W^T in place, then Y = RMSNorm(X) * norm_w; returns Y."""
+    M, K = A.shape
+    N = W.shape[0]
+    Y = _torch().empty_like(X) if Y is None else Y
+    need = lib().medusa_gemm_resid_rmsnorm_workspace_size(dtype_code(A), M, N, K)
+    ws = L._ws(ws, need, A.device)
+    check(lib().medusa_gemm_resid_rmsnorm(dtype_code(A), M, N, K, ptr(A), A.stride(0), ptr(W), ptr(X), ptr(norm_w),
+                                          float(eps), ptr(Y), ptr(ws), ws.numel(), stream_ptr()))
+    return Y
+
+
 def argmax_rows(x, out=None):
     torch = _torch()
     M, V = x.shape

@@ -71,4 +71,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// bf16 RMSNorm of M rows of length N (N % 8 == 0, N <= 8192, 16-byte aligned
+// rows), optionally after adding SK fp32 split-K partials [SK][M][N] into x
+// (gemm.hip).
+int resid_rmsnorm_bf16(int M, int N, int SK, const float* part, bf16_t* x, const bf16_t* g, float eps, bf16_t* y,
+                       hipStream_t stream);
+
 }  // namespace medusa

@@ -135,6 +135,9 @@ extern "C" int medusa_rmsnorm(int dtype, int M, int N, const void* x, const void
   MEDUSA_REQUIRE(M >= 0 && N > 0, MEDUSA_ERR_ARG, "rmsnorm: bad sizes");
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(x && w && y, MEDUSA_ERR_ARG, "rmsnorm: null pointer");
+  const bool vec_ok = N % 8 == 0 && N <= 8192 && (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15) == 0;
+  if (dtype == MEDUSA_BF16 && vec_ok)
+    return resid_rmsnorm_bf16(M, N, 0, nullptr, (bf16_t*)x, (const bf16_t*)w, eps, (bf16_t*)y, stream);
   if (dtype == MEDUSA_F32)
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, stream, N, (const float*)x, (const float*)w, eps,
                        (float*)y);

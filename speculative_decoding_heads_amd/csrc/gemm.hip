@@ -42,6 +42,7 @@ struct EpiArgs {
   const void* A;  // for MEDUSA_EPI_SILU_RESID_A
   int64_t lda;
   int K;
+  int part_only;  // bf16 kernels: always leave fp32 partials (a fused consumer reduces them)
 };
 
 // Apply the epilogue to a pair-capable element set: value v at (m, n).  For
@@ -133,7 +134,7 @@ template <int NR, int MB>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[NR][MB], int n0, int m0, int M, int N, int SK, int ks,
                                            int bz, const EpiArgs& e, int64_t sC, int64_t sR, const bf16_t* A,
                                            float* __restrict__ part, int l16, int lg) {
-  if (SK > 1) {
+  if (SK > 1 || e.part_only) {
     float* pp = part + (((size_t)bz * SK + ks) * M) * N;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
@@ -549,45 +550,15 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
     const int skmax = nchunks / (2 * per_wg) > 0 ? nchunks / (2 * per_wg) : 1;
     p.SK = sk < 1 ? 1 : (sk > skmax ? skmax : sk);
   }
-  p.part_bytes = p.SK > 1 ? align_up((size_t)batch * p.SK * M * N * sizeof(float), 256) : 0;
+  p.part_bytes = align_up((size_t)batch * p.SK * M * N * sizeof(float), 256);
+  if (p.SK == 1) p.part_bytes = 0;
   return p;
 }
 
-}  // namespace
-
-extern "C" size_t medusa_gemm_workspace_size(int dtype, int M, int N, int K, int batch) {
-  if (dtype != MEDUSA_BF16 || M <= 0 || N <= 0 || K <= 0 || batch <= 0 || K % GK) return 0;
-  return gemm_plan(M, N, K, batch).part_bytes;
-}
-
-extern "C" int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_t lda, int64_t strideA, const void* W,
-                           int64_t strideW, void* C, int64_t ldc, int64_t strideC, int batch, int epilogue,
-                           const void* R, int64_t ldr, int64_t strideR, void* ws, size_t ws_bytes,
-                           hipStream_t stream) {
-  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "gemm: dtype %d", dtype);
-  MEDUSA_REQUIRE(M >= 0 && N > 0 && K > 0 && batch >= 1, MEDUSA_ERR_ARG, "gemm: bad sizes M=%d N=%d K=%d", M, N, K);
-  MEDUSA_REQUIRE(epilogue >= MEDUSA_EPI_F32 && epilogue <= MEDUSA_EPI_SWIGLU, MEDUSA_ERR_ARG, "gemm: epilogue %d",
-                 epilogue);
-  MEDUSA_REQUIRE(epilogue != MEDUSA_EPI_RESID || R, MEDUSA_ERR_ARG, "gemm: residual epilogue needs R");
-  MEDUSA_REQUIRE(epilogue != MEDUSA_EPI_SWIGLU || N % 2 == 0, MEDUSA_ERR_ARG, "gemm: SwiGLU needs even N");
-  MEDUSA_REQUIRE(epilogue != MEDUSA_EPI_SILU_RESID_A || lda >= K, MEDUSA_ERR_ARG, "gemm: bad lda");
-  MEDUSA_REQUIRE(lda >= K, MEDUSA_ERR_ARG, "gemm: lda < K");
-  if (M == 0) return MEDUSA_OK;
-  MEDUSA_REQUIRE(A && W && C, MEDUSA_ERR_ARG, "gemm: null pointer");
-  EpiArgs e{epilogue, C, ldc, R, ldr, A, lda, K};
-  if (dtype == MEDUSA_F32) {
-    const int nout = epilogue == MEDUSA_EPI_SWIGLU ? N / 2 : N;
-    dim3 grid((nout + 63) / 64, (M + 3) / 4, batch);
-    hipLaunchKernelGGL(gemm_valu_kernel<float>, grid, dim3(64, 4), 0, stream, M, N, K, (const float*)A, lda, strideA,
-                       (const float*)W, strideW, e, strideC, strideR);
-    return check_launch("gemm fp32");
-  }
-  MEDUSA_REQUIRE(K % GK == 0, MEDUSA_ERR_UNSUPPORTED, "gemm: bf16 needs K %% 32 == 0 (K=%d)", K);
-  MEDUSA_REQUIRE(lda % 8 == 0 && strideA % 8 == 0 && strideW % 8 == 0, MEDUSA_ERR_UNSUPPORTED,
-                 "gemm: bf16 rows must be 16-byte aligned");
-  GemmPlan p = gemm_plan(M, N, K, batch);
-  MEDUSA_REQUIRE(ws_bytes >= p.part_bytes && (p.SK == 1 || ws), MEDUSA_ERR_WORKSPACE, "gemm: workspace %zu < %zu",
-                 ws_bytes, p.part_bytes);
+// Launch the bf16 product kernel of plan p (partials, when left, go to ws).
+void gemm_bf16_launch(const GemmPlan& p, int M, int N, int K, const void* A, int64_t lda, int64_t strideA,
+                      const void* W, int64_t strideW, const EpiArgs& e, int64_t strideC, int64_t strideR, void* ws,
+                      int batch, hipStream_t stream) {
   dim3 grid(p.n_tiles, p.m_tiles * p.SK, batch);
 #define GEMM_LAUNCH_KW(MBV, NRV, UV, KWV)                                                                      \
   hipLaunchKernelGGL((gemm_bf16_kernel<MBV, NRV, UV, KWV>), grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, \
@@ -641,6 +612,44 @@ extern "C" int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_
 #undef GEMM_LAUNCH_LDS_G
 #undef GEMM_LAUNCH_LDS_U
 #undef GEMM_LAUNCH_LDS_K
+}
+
+}  // namespace
+
+extern "C" size_t medusa_gemm_workspace_size(int dtype, int M, int N, int K, int batch) {
+  if (dtype != MEDUSA_BF16 || M <= 0 || N <= 0 || K <= 0 || batch <= 0 || K % GK) return 0;
+  return gemm_plan(M, N, K, batch).part_bytes;
+}
+
+extern "C" int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_t lda, int64_t strideA, const void* W,
+                           int64_t strideW, void* C, int64_t ldc, int64_t strideC, int batch, int epilogue,
+                           const void* R, int64_t ldr, int64_t strideR, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "gemm: dtype %d", dtype);
+  MEDUSA_REQUIRE(M >= 0 && N > 0 && K > 0 && batch >= 1, MEDUSA_ERR_ARG, "gemm: bad sizes M=%d N=%d K=%d", M, N, K);
+  MEDUSA_REQUIRE(epilogue >= MEDUSA_EPI_F32 && epilogue <= MEDUSA_EPI_SWIGLU, MEDUSA_ERR_ARG, "gemm: epilogue %d",
+                 epilogue);
+  MEDUSA_REQUIRE(epilogue != MEDUSA_EPI_RESID || R, MEDUSA_ERR_ARG, "gemm: residual epilogue needs R");
+  MEDUSA_REQUIRE(epilogue != MEDUSA_EPI_SWIGLU || N % 2 == 0, MEDUSA_ERR_ARG, "gemm: SwiGLU needs even N");
+  MEDUSA_REQUIRE(epilogue != MEDUSA_EPI_SILU_RESID_A || lda >= K, MEDUSA_ERR_ARG, "gemm: bad lda");
+  MEDUSA_REQUIRE(lda >= K, MEDUSA_ERR_ARG, "gemm: lda < K");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(A && W && C, MEDUSA_ERR_ARG, "gemm: null pointer");
+  EpiArgs e{epilogue, C, ldc, R, ldr, A, lda, K, 0};
+  if (dtype == MEDUSA_F32) {
+    const int nout = epilogue == MEDUSA_EPI_SWIGLU ? N / 2 : N;
+    dim3 grid((nout + 63) / 64, (M + 3) / 4, batch);
+    hipLaunchKernelGGL(gemm_valu_kernel<float>, grid, dim3(64, 4), 0, stream, M, N, K, (const float*)A, lda, strideA,
+                       (const float*)W, strideW, e, strideC, strideR);
+    return check_launch("gemm fp32");
+  }
+  MEDUSA_REQUIRE(K % GK == 0, MEDUSA_ERR_UNSUPPORTED, "gemm: bf16 needs K %% 32 == 0 (K=%d)", K);
+  MEDUSA_REQUIRE(lda % 8 == 0 && strideA % 8 == 0 && strideW % 8 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "gemm: bf16 rows must be 16-byte aligned");
+  GemmPlan p = gemm_plan(M, N, K, batch);
+  MEDUSA_REQUIRE(ws_bytes >= p.part_bytes && (p.SK == 1 || ws), MEDUSA_ERR_WORKSPACE, "gemm: workspace %zu < %zu",
+                 ws_bytes, p.part_bytes);
+  gemm_bf16_launch(p, M, N, K, A, lda, strideA, W, strideW, e, strideC, strideR, ws, batch, stream);
   int rc = check_launch("gemm bf16");
   if (rc) return rc;
   if (p.SK > 1) {
@@ -651,4 +660,128 @@ extern "C" int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_
     return check_launch("gemm split-K reduce");
   }
   return MEDUSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Residual add + RMSNorm fused with the product's split-K reduction
+// ---------------------------------------------------------------------------
+namespace {
+
+// One 256-thread block per row; each thread holds NV vectors of 8 columns.
+// SK > 0: acc = sum_s part[s][m][:] in split order, x[m,:] = bf16(x[m,:] + acc)
+// is stored; SK == 0: x is only read.  Then y[m,:] = bf16(x[m,:] * inv * g)
+// with inv = 1 / sqrt(mean(x[m,:]^2) + eps) taken over the stored bf16 x.
+template <int NV>
+__global__ __launch_bounds__(256) void resid_rmsnorm_kernel(int M, int N, int SK, const float* __restrict__ part,
+                                                            bf16_t* __restrict__ x, const bf16_t* __restrict__ g,
+                                                            float eps, bf16_t* __restrict__ y) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int m = blockIdx.x, tid = threadIdx.x;
+  bf16_t* xr = x + (size_t)m * N;
+  float v[NV][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int n = (q * 256 + tid) * 8;
+    if (n >= N) continue;
+    const u32x4 raw = *(const u32x4*)(xr + n);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[q][2 * i] = __uint_as_float(raw[i] << 16);
+      v[q][2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
+    }
+    if (SK > 0) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int sp = 0; sp < SK; ++sp) {
+        const float4* pp = (const float4*)(part + ((size_t)sp * M + m) * N + n);
+        const float4 a = pp[0], b = pp[1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      }
+      u32x4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16_t lo = f32_to_bf16(v[q][2 * i] + acc[2 * i]);
+        const bf16_t hi = f32_to_bf16(v[q][2 * i + 1] + acc[2 * i + 1]);
+        v[q][2 * i] = bf16_to_f32(lo);
+        v[q][2 * i + 1] = bf16_to_f32(hi);
+        out[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+      *(u32x4*)(xr + n) = out;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += v[q][i] * v[q][i];
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int n = (q * 256 + tid) * 8;
+    if (n >= N) continue;
+    const u32x4 graw = *(const u32x4*)(g + n);
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g0 = __uint_as_float(graw[i] << 16), g1 = __uint_as_float(graw[i] & 0xffff0000u);
+      out[i] = (uint32_t)f32_to_bf16(v[q][2 * i] * inv * g0) | ((uint32_t)f32_to_bf16(v[q][2 * i + 1] * inv * g1) << 16);
+    }
+    *(u32x4*)(y + (size_t)m * N + n) = out;
+  }
+}
+
+}  // namespace
+
+namespace medusa {
+
+// bf16 RMSNorm rows of x (optionally after adding SK fp32 partials); N % 8 == 0, N <= 8192.
+int resid_rmsnorm_bf16(int M, int N, int SK, const float* part, bf16_t* x, const bf16_t* g, float eps, bf16_t* y,
+                       hipStream_t stream) {
+  MEDUSA_REQUIRE(N % 8 == 0 && N <= 8192, MEDUSA_ERR_UNSUPPORTED, "rmsnorm bf16: N=%d (need N %% 8 == 0, <= 8192)", N);
+  if (M == 0) return MEDUSA_OK;
+  const int nv = (N + 2047) / 2048;
+  if (nv == 1)
+    hipLaunchKernelGGL(resid_rmsnorm_kernel<1>, dim3(M), dim3(256), 0, stream, M, N, SK, part, x, g, eps, y);
+  else if (nv == 2)
+    hipLaunchKernelGGL(resid_rmsnorm_kernel<2>, dim3(M), dim3(256), 0, stream, M, N, SK, part, x, g, eps, y);
+  else
+    hipLaunchKernelGGL(resid_rmsnorm_kernel<4>, dim3(M), dim3(256), 0, stream, M, N, SK, part, x, g, eps, y);
+  return check_launch("resid_rmsnorm");
+}
+
+}  // namespace medusa
+
+extern "C" size_t medusa_gemm_resid_rmsnorm_workspace_size(int dtype, int M, int N, int K) {
+  if (dtype != MEDUSA_BF16 || M <= 0 || N <= 0 || K <= 0 || K % GK) return 0;
+  const GemmPlan p = gemm_plan(M, N, K, 1);
+  return align_up((size_t)p.SK * M * N * sizeof(float), 256);
+}
+
+extern "C" int medusa_gemm_resid_rmsnorm(int dtype, int M, int N, int K, const void* A, int64_t lda, const void* W,
+                                         void* X, const void* norm_w, float eps, void* Y, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "gemm_resid_rmsnorm: dtype %d", dtype);
+  MEDUSA_REQUIRE(M >= 0 && N > 0 && K > 0 && lda >= K, MEDUSA_ERR_ARG, "gemm_resid_rmsnorm: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(A && W && X && norm_w && Y, MEDUSA_ERR_ARG, "gemm_resid_rmsnorm: null pointer");
+  if (dtype == MEDUSA_F32) {
+    int rc = medusa_gemm(dtype, M, N, K, A, lda, 0, W, 0, X, N, 0, 1, MEDUSA_EPI_RESID, X, N, 0, nullptr, 0, stream);
+    if (rc) return rc;
+    return medusa_rmsnorm(dtype, M, N, X, norm_w, eps, Y, stream);
+  }
+  MEDUSA_REQUIRE(K % GK == 0 && lda % 8 == 0 && N % 8 == 0 && N <= 8192, MEDUSA_ERR_UNSUPPORTED,
+                 "gemm_resid_rmsnorm: bf16 needs K %% 32 == 0, 16-byte rows, N %% 8 == 0 and N <= 8192");
+  const GemmPlan p = gemm_plan(M, N, K, 1);
+  const size_t need = align_up((size_t)p.SK * M * N * sizeof(float), 256);
+  MEDUSA_REQUIRE(ws && ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "gemm_resid_rmsnorm: workspace %zu < %zu", ws_bytes,
+                 need);
+  EpiArgs e{MEDUSA_EPI_F32, nullptr, N, nullptr, 0, A, lda, K, 1};
+  gemm_bf16_launch(p, M, N, K, A, lda, 0, W, 0, e, 0, 0, ws, 1, stream);
+  int rc = check_launch("gemm_resid_rmsnorm product");
+  if (rc) return rc;
+  return resid_rmsnorm_bf16(M, N, p.SK, (const float*)ws, (bf16_t*)X, (const bf16_t*)norm_w, eps, (bf16_t*)Y, stream);
 }

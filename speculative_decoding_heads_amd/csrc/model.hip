@@ -79,6 +79,8 @@ size_t gemm_ws_max(const medusa_model* m, int M) {
   upd(medusa_gemm_workspace_size(m->dtype, M, 2 * F, d, 1));
   upd(medusa_gemm_workspace_size(m->dtype, M, d, F, 1));
   upd(medusa_gemm_workspace_size(m->dtype, M, V, d, 1));
+  upd(medusa_gemm_resid_rmsnorm_workspace_size(m->dtype, M, d, Hq * Dh));
+  upd(medusa_gemm_resid_rmsnorm_workspace_size(m->dtype, M, d, F));
   return w;
 }
 
@@ -150,11 +152,14 @@ extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t
     if (r_) return r_; \
   } while (0)
   CK(medusa_embed(dt, M, d, tokens, m->embed, m->vocab, f.x, stream));
+  // each residual projection also applies the RMSNorm that feeds the next
+  // sub-layer (the last one the final norm, into h)
+  CK(medusa_rmsnorm(dt, M, d, f.x, m->layers[0].attn_norm, m->norm_eps, f.xn, stream));
   for (int l = 0; l < m->n_layers; ++l) {
     const medusa_layer_weights& w = m->layers[l];
+    const bool last = l + 1 == m->n_layers;
     char* kt = (char*)Kt + l * side_layer;
     char* vt = (char*)Vt + l * side_layer;
-    CK(medusa_rmsnorm(dt, M, d, f.x, w.attn_norm, m->norm_eps, f.xn, stream));
     CK(medusa_gemm(dt, M, (Hq + 2 * Hkv) * Dh, d, f.xn, d, 0, w.wqkv, 0, f.qkv, (Hq + 2 * Hkv) * Dh, 0, 1,
                    MEDUSA_EPI_F32, nullptr, 0, 0, f.gws, f.gws_bytes, stream));
     CK(medusa_rope_split(dt, B, T, Hq, Hkv, Dh, (const float*)f.qkv, pos, m->rope_cos, m->rope_sin, m->rope_max_pos,
@@ -162,15 +167,13 @@ extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t
     CK(tree_attention(dt, B, T, Hq, Hkv, Dh, f.q, Lmax ? (const char*)Kc + l * cache_layer : nullptr,
                       Lmax ? (const char*)Vc + l * cache_layer : nullptr, Lmax, L_hint, seq_len, kt, vt, anc, scale,
                       f.attn, f.aws, f.aws_bytes, stream));
-    CK(medusa_gemm(dt, M, d, Hq * Dh, f.attn, Hq * Dh, 0, w.wo, 0, f.x, d, 0, 1, MEDUSA_EPI_RESID, f.x, d, 0, f.gws,
-                   f.gws_bytes, stream));
-    CK(medusa_rmsnorm(dt, M, d, f.x, w.ffn_norm, m->norm_eps, f.xn, stream));
+    CK(medusa_gemm_resid_rmsnorm(dt, M, d, Hq * Dh, f.attn, Hq * Dh, w.wo, f.x, w.ffn_norm, m->norm_eps, f.xn, f.gws,
+                                 f.gws_bytes, stream));
     CK(medusa_gemm(dt, M, 2 * F, d, f.xn, d, 0, w.w_gate_up, 0, f.act, F, 0, 1, MEDUSA_EPI_SWIGLU, nullptr, 0, 0,
                    f.gws, f.gws_bytes, stream));
-    CK(medusa_gemm(dt, M, d, F, f.act, F, 0, w.w_down, 0, f.x, d, 0, 1, MEDUSA_EPI_RESID, f.x, d, 0, f.gws,
-                   f.gws_bytes, stream));
+    CK(medusa_gemm_resid_rmsnorm(dt, M, d, F, f.act, F, w.w_down, f.x, last ? m->final_norm : m->layers[l + 1].attn_norm,
+                                 m->norm_eps, last ? h : f.xn, f.gws, f.gws_bytes, stream));
   }
-  CK(medusa_rmsnorm(dt, M, d, f.x, m->final_norm, m->norm_eps, h, stream));
   CK(medusa_gemm(dt, M, m->vocab, d, h, d, 0, m->lm_head, 0, logits, m->vocab, 0, 1, MEDUSA_EPI_F32, nullptr, 0, 0,
                  f.gws, f.gws_bytes, stream));
   return MEDUSA_OK;

@@ -201,7 +201,7 @@ def test_heads_topk_fp32_small(dev):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (8, 1000, 512), (64, 12288, 4096), (64, 4096, 11008),
-                                   (100, 384, 256), (512, 512, 4096)])
+                                   (100, 384, 256), (512, 512, 4096), (40, 1000, 1056), (33, 200, 96)])
 def test_gemm_bf16(dev, M, N, K):
     import torch
     from speculative_decoding_heads_amd import api
@@ -246,6 +246,33 @@ def test_gemm_epilogues(dev, dtype_name):
     z = A.astype(np.float64) @ Wsq.astype(np.float64).T
     assert_close(to_np(out), np.concatenate([A, A], 1) + silu(z), what="silu_resid", **tol)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype_name,M,N,K", [("bf16", 64, 4096, 4096), ("bf16", 64, 4096, 11008),
+                                              ("bf16", 5, 512, 256), ("bf16", 40, 1000, 1056),
+                                              ("fp32", 5, 512, 256)])
+def test_gemm_resid_rmsnorm(dev, dtype_name, M, N, K):
+    import torch
+    from oracle.decoder import rmsnorm
+    from speculative_decoding_heads_amd import api
+    from workloads import bf16_round
+    say("gemm_resid_rmsnorm", dtype_name, M, N, K)
+    tdt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    rnd = bf16_round if dtype_name == "bf16" else (lambda x: x)
+    tol = dict(rtol=2e-2, atol=1e-2) if dtype_name == "bf16" else dict(rtol=1e-5, atol=1e-5)
+    rng = np.random.default_rng(M * 7 + K)
+    A = rnd(rng.standard_normal((M, K)).astype(np.float32))
+    W = rnd((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    X = rnd(rng.standard_normal((M, N)).astype(np.float32))
+    g = rnd((1.0 + 0.1 * rng.standard_normal(N)).astype(np.float32))
+    gX = to_dev(X, tdt, dev)
+    Y = api.gemm_resid_rmsnorm(to_dev(A, tdt, dev), to_dev(W, tdt, dev), gX, to_dev(g, tdt, dev), 1e-6)
+    torch.cuda.synchronize()
+    x_ref = X.astype(np.float64) + A.astype(np.float64) @ W.astype(np.float64).T
+    assert_close(to_np(gX), x_ref, what="residual", **tol)
+    # the norm is taken over the stored residual, so compare it against that
+    y_ref = rmsnorm(to_np(gX).astype(np.float64), g)
+    assert_close(to_np(Y), y_ref, what="norm", **tol)
 
 
 def test_argmax_and_topk_rows_ties(dev):
