@@ -131,20 +131,21 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float*
 }
 
 struct MfmaPlan {
-  int n_rchunks, n_splits;
+  int nw, n_rchunks, n_splits;
   size_t ws_o_bytes, ws_ml_bytes;
 };
 
 MfmaPlan mfma_plan(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint) {
   MfmaPlan p;
   const int R = T * (Hq / Hkv);
-  const int rows_wg = attn_stream_rows_per_wg();
+  p.nw = attn_stream_waves(R);
+  const int rows_wg = 32 * p.nw;
   p.n_rchunks = (R + rows_wg - 1) / rows_wg;
   const int64_t tiles = (L_hint + ATTN_KT - 1) / ATTN_KT;
   const int64_t units = (int64_t)B * Hkv * p.n_rchunks;
-  // aim at one workgroup per CU (256 CUs), each split at least 4 tiles
-  int64_t s = (256 + units - 1) / units;
-  const int64_t smax = (tiles + 3) / 4;
+  // aim at ~8 waves per CU (256 CUs), each split at least 2 tiles
+  int64_t s = (2048 / p.nw + units - 1) / units;
+  const int64_t smax = (tiles + 1) / 2;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
   p.n_splits = (int)s;
@@ -188,7 +189,7 @@ extern "C" int tree_attention(int dtype, int B, int T, int Hq, int Hkv, int Dh, 
     float* ws_ml = p.n_splits > 1 ? (float*)((char*)ws + p.ws_o_bytes) : nullptr;
     const float sl2 = scale * 1.4426950408889634f;
     dim3 grid(p.n_splits, Hkv, B * p.n_rchunks);
-    int rc = launch_attn_stream(Dh, grid, stream, (const bf16_t*)q, (const bf16_t*)Kc, (const bf16_t*)Vc, Lmax, seq_len,
+    int rc = launch_attn_stream(Dh, p.nw, grid, stream, (const bf16_t*)q, (const bf16_t*)Kc, (const bf16_t*)Vc, Lmax, seq_len,
                                 (const bf16_t*)Kt, (const bf16_t*)Vt, anc, T, Hq, Hkv, p.n_rchunks, sl2, p.n_splits,
                                 (bf16_t*)out, ws_o, ws_ml);
     if (rc) return rc;

@@ -6,12 +6,13 @@ namespace medusa {
 
 constexpr int ATTN_KT = 64;  // keys per tile
 
-// Query rows one workgroup serves (32 per wave) for the configured variant.
-int attn_stream_rows_per_wg();
+// Waves per workgroup (32 query rows each) for R query rows per KV head.
+int attn_stream_waves(int R);
 
-// grid = (n_splits, Hkv, B * n_rchunks); ws_o / ws_ml used only when n_splits > 1.
-int launch_attn_stream(int Dh, dim3 grid, hipStream_t stream, const bf16_t* q, const bf16_t* Kc, const bf16_t* Vc,
-                       int64_t Lmax, const int32_t* seq_len, const bf16_t* Kt, const bf16_t* Vt,
+// nw waves per workgroup (2, 4 or 8); grid = (n_splits, Hkv, B * n_rchunks)
+// with n_rchunks = ceil(R / (32 * nw)); ws_o / ws_ml used only when n_splits > 1.
+int launch_attn_stream(int Dh, int nw, dim3 grid, hipStream_t stream, const bf16_t* q, const bf16_t* Kc,
+                       const bf16_t* Vc, int64_t Lmax, const int32_t* seq_len, const bf16_t* Kt, const bf16_t* Vt,
                        const uint64_t* anc, int T, int Hq, int Hkv, int n_rchunks, float scale_log2, int n_splits,
                        bf16_t* out, float* ws_o, float* ws_ml);
 

@@ -5,8 +5,8 @@
 // Medusa", section 一.2: a node only sees its predecessors; section 二.3: the
 // prefix stays visible) times V.
 //
-// One workgroup of 8 waves per (sequence, KV head, chunk of <= 256 query rows,
-// KV split).  The T*G query rows sharing a KV head (G = Hq/Hkv) are all served
+// One workgroup of NW <= 8 waves per (sequence, KV head, chunk of <= 32*NW
+// query rows, KV split).  The T*G query rows sharing a KV head (G = Hq/Hkv) are all served
 // by a single pass over that head's keys, so K/V bytes are read from HBM once
 // per KV head no matter how many query heads share them.  Wave w owns the
 // 32-row block w:
@@ -24,7 +24,6 @@
 // With several KV splits each workgroup writes fp32 partials (O, m, l) that
 // attn_combine merges.
 #include <stdlib.h>
-#include <string.h>
 
 #include <type_traits>
 
@@ -185,7 +184,11 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
         h[e] = (d & 1) ? (word >> 16) : (word & 0xffffu);
       }
       bf16_t* dst = &sm.v[buf][(vch * 8 + d) * VP + vkg * KPT];
-      if constexpr (KPT == 4) {
+      if constexpr (KPT == 8) {
+        // V^T rows are 8-byte aligned (pitch 68 elements)
+        *(uint2*)dst = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        *(uint2*)(dst + 4) = make_uint2(h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      } else if constexpr (KPT == 4) {
         *(uint2*)dst = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       } else if constexpr (KPT == 2) {
         *(uint32_t*)dst = h[0] | (h[1] << 16);
@@ -340,21 +343,18 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
 
 }  // namespace
 
-// Variant: 8 waves x 32 rows with two register tiles in flight (default), or
-// 4 waves x 32 rows (two workgroups per CU) with one or two; MEDUSA_ATTN_VARIANT
-// = "8x2" | "4x1" | "4x2" selects one for tuning runs.
-static int variant() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("MEDUSA_ATTN_VARIANT");
-    v = 0;
-    if (e && !strcmp(e, "4x1")) v = 1;
-    if (e && !strcmp(e, "4x2")) v = 2;
-  }
-  return v;
+// Waves per workgroup: one per 32-row block of the rows sharing a KV head, up
+// to 8 (R <= 64 -> 2, R <= 128 -> 4, else 8), always with two register tiles in
+// flight.  MEDUSA_ATTN_WAVES = 2 | 4 | 8 forces a width for tuning runs.
+int attn_stream_waves(int R) {
+  static const int forced = [] {
+    const char* e = getenv("MEDUSA_ATTN_WAVES");
+    const int v = e ? atoi(e) : 0;
+    return v == 2 || v == 4 || v == 8 ? v : 0;
+  }();
+  if (forced) return forced;
+  return R <= 64 ? 2 : (R <= 128 ? 4 : 8);
 }
-
-int attn_stream_rows_per_wg() { return variant() == 0 ? 256 : 128; }
 
 template <int NW, int PF>
 static void launch_v(int Dh, dim3 grid, hipStream_t stream, const bf16_t* q, const bf16_t* Kc, const bf16_t* Vc,
@@ -369,24 +369,20 @@ static void launch_v(int Dh, dim3 grid, hipStream_t stream, const bf16_t* q, con
                        Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2, n_splits, out, ws_o, ws_ml);
 }
 
-int launch_attn_stream(int Dh, dim3 grid, hipStream_t stream, const bf16_t* q, const bf16_t* Kc, const bf16_t* Vc,
-                       int64_t Lmax, const int32_t* seq_len, const bf16_t* Kt, const bf16_t* Vt,
+int launch_attn_stream(int Dh, int nw, dim3 grid, hipStream_t stream, const bf16_t* q, const bf16_t* Kc,
+                       const bf16_t* Vc, int64_t Lmax, const int32_t* seq_len, const bf16_t* Kt, const bf16_t* Vt,
                        const uint64_t* anc, int T, int Hq, int Hkv, int n_rchunks, float scale_log2, int n_splits,
                        bf16_t* out, float* ws_o, float* ws_ml) {
   if (Dh != 128 && Dh != 64) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: streaming kernel takes Dh 64 or 128");
-  switch (variant()) {
-    case 1:
-      launch_v<4, 1>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
-                     n_splits, out, ws_o, ws_ml);
-      break;
-    case 2:
-      launch_v<4, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
-                     n_splits, out, ws_o, ws_ml);
-      break;
-    default:
-      launch_v<8, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
-                     n_splits, out, ws_o, ws_ml);
-  }
+  if (nw == 2)
+    launch_v<2, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
+                   n_splits, out, ws_o, ws_ml);
+  else if (nw == 4)
+    launch_v<4, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
+                   n_splits, out, ws_o, ws_ml);
+  else
+    launch_v<8, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
+                   n_splits, out, ws_o, ws_ml);
   return check_launch("tree_attention stream");
 }
 

@@ -24,6 +24,8 @@
 // SwiGLU on row-interleaved gate/up weights (row 2j = gate j, row 2j+1 = up j).
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "medusa_model.h"
 
@@ -225,8 +227,13 @@ __global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, co
     F8 a[U][MB];
   };
   Stage S0, S1;
+  // tiles start their k walk at different chunks (see gemm_lds_kernel)
+  const int nck = c1 - c0;
+  const int rot = nck > 0 ? (int)(((unsigned)nt * 37u) % (unsigned)nck) : 0;
   auto load = [&](Stage& s, int c) {
-    const int k = c * U * GK;
+    int y = c - c0 + rot;
+    if (y >= nck) y -= nck;
+    const int k = (c0 + y) * U * GK;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -290,62 +297,68 @@ __global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, co
   store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
 }
 
-// Kernel for M > 32.  The four waves of a workgroup form KG k-groups of 4/KG
-// waves; the waves of a k-group own neighbouring (NR*16)-row W tiles and walk
-// the same k range, and each k-group stages the 64 A rows of its current chunk
-// (U k-steps) once in LDS, so A costs one global read per k-group instead of
-// one per wave (re-reading A per wave caps these products at about half the
-// HBM rate).  W fragments go straight from global memory to registers, NS
-// chunks ahead; A goes global -> registers -> LDS one chunk ahead through two
-// LDS buffers per k-group, with one barrier per chunk.  Staged rows are padded
-// by 16 bytes so the 16 rows that one ds_read_b128 touches fall in distinct
-// banks.  The k-groups are summed through LDS in group order at the end; a
-// K split across workgroups (SK > 1) leaves fp32 partials for
-// splitk_reduce_kernel.  grid (N tiles of (4/KG)*NR*16 rows, m tiles * SK, batch).
-template <int NR, int U, int NS, int KG>
+// Kernel for M > 32.  The four waves of a workgroup own neighbouring
+// (NR*16)-row W tiles and walk the same k range; the workgroup stages the 64 A
+// rows of each chunk (U k-steps) once in LDS, so A costs one global read per
+// workgroup instead of one per wave (re-reading A per wave caps these products
+// at about half the HBM rate).  Per chunk and wave:
+//   * W fragments go straight from global memory to registers, NS chunks ahead;
+//   * A goes global -> registers (NS chunks ahead) -> LDS two chunks ahead,
+//     through three LDS buffers, with one barrier per chunk;
+//   * the A fragments of the next chunk are read from LDS before the current
+//     chunk's MFMAs are issued, so LDS latency hides behind them (with one
+//     workgroup per CU there is no other wave to cover it).
+// Staged rows are padded by 16 bytes so the 16 rows that one ds_read_b128
+// touches fall in distinct banks.  A K split across workgroups (SK > 1) leaves
+// fp32 partials.  grid (N tiles of 4*NR*16 rows, m tiles * SK, batch).
+template <int NR, int U, int NS>
 __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, const bf16_t* __restrict__ A, int64_t lda,
                                                         int64_t sA, const bf16_t* __restrict__ W, int64_t sW, int SK,
                                                         EpiArgs e, int64_t sC, int64_t sR, float* __restrict__ part) {
-  constexpr int MB = 4, TN = NR * 16, TM = MB * 16;
-  constexpr int NG = 4 / KG;               // waves per k-group
-  constexpr int ROWB = U * GK * 2 + 16;    // bytes per staged A row
-  constexpr int PPR = U * GK * 2 / 16;     // 16-byte pieces per A row and chunk
-  constexpr int PPT = GM * PPR / (NG * 64);  // pieces per thread and chunk
+  constexpr int MB = 4, TN = NR * 16;
+  constexpr int ROWB = U * GK * 2 + 16;  // bytes per staged A row
+  constexpr int PPR = U * GK * 2 / 16;   // 16-byte pieces per A row and chunk
+  constexpr int PPT = GM * PPR / GTHR;   // pieces per thread and chunk (= U)
   constexpr int BUFB = GM * ROWB;
-  constexpr int A_BYTES = KG * 2 * BUFB;
-  constexpr int R_BYTES = KG > 1 ? (KG - 1) * NG * TN * TM * 4 : 0;
-  __shared__ __align__(16) char lds[A_BYTES > R_BYTES ? A_BYTES : R_BYTES];
+  static_assert(NS == 4, "the step sequence below is written for four register stages");
+  __shared__ __align__(16) char lds[3 * BUFB];
   const int bz = blockIdx.z;
   const int nt = blockIdx.x;
   const int mt = blockIdx.y / SK;
   const int ks = blockIdx.y % SK;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int kg = w / NG, ng = w % NG, gtid = tid - kg * NG * 64;
   A += bz * sA;
   W += bz * sW;
-  const int n0 = (nt * NG + ng) * TN, m0 = mt * GM;
+  const int n0 = (nt * 4 + w) * TN, m0 = mt * GM;
   const int nchunks = (K / GK) / U;
   const int c0 = (int)((int64_t)nchunks * ks / SK), c1 = (int)((int64_t)nchunks * (ks + 1) / SK);
-  // every k-group runs `per` pipeline steps (uniform over the workgroup, so
-  // all waves meet the same barriers); its real chunks are [g0, g1)
-  const int per = (c1 - c0 + KG - 1) / KG;
-  const int g0 = c0 + kg * per, g1 = min(g0 + per, c1);
-  auto clampc = [&](int v) { return max(min(g0 + v, g1 - 1), 0); };
-  char* albase = lds + kg * 2 * BUFB;
+  const int per = c1 - c0;  // chunks of this workgroup (uniform)
+  // Workgroups start their k walk at different chunks (rotated by the W tile
+  // index): walking in step, all of them would hit the same column offset of
+  // their W rows at once and crowd the same memory channels.  Workgroups of one
+  // W tile (several m tiles) keep the same order so they share its lines in
+  // L2.  The rotation only changes the order of the k sum, fixed for a shape.
+  const int rot = per > 0 ? (int)(((unsigned)nt * 37u) % (unsigned)per) : 0;
+  auto clampc = [&](int x) {
+    int y = min(x, per - 1) + rot;
+    if (y >= per) y -= per;
+    return c0 + y;
+  };
 
   const bf16_t* wrow[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) wrow[i] = W + (size_t)min(n0 + i * 16 + l16, N - 1) * K + lg * 8;
-  // a k-group's NG*64 threads stage GM * PPR pieces: thread gtid takes gtid + NG*64*q
+  // GM * PPR pieces per chunk: thread tid stages pieces tid + GTHR*q
   const bf16_t* apiece[PPT];
   int aoff[PPT];
 #pragma unroll
   for (int q = 0; q < PPT; ++q) {
-    const int pc = gtid + NG * 64 * q, r = pc / PPR, cp = pc % PPR;
+    const int pc = tid + GTHR * q, r = pc / PPR, cp = pc % PPR;
     apiece[q] = A + (size_t)min(m0 + r, M - 1) * lda + cp * 8;
     aoff[q] = r * ROWB + cp * 16;
   }
+  const int boff = l16 * ROWB + lg * 16;  // this lane's A fragment within a 16-row block
   f32x4 acc[NR][MB];
 #pragma unroll
   for (int i = 0; i < NR; ++i)
@@ -360,6 +373,7 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
     u32x4 a[PPT];
   };
   Stage S[NS];
+  F8 B[2][U][MB];  // A fragments of the current and the next chunk
   // A pieces are issued before W so waiting for them does not wait for W
   auto gload = [&](Stage& st, int c) {
     const int k = c * U * GK;
@@ -372,84 +386,65 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
   };
   auto stage = [&](int buf, const Stage& st) {
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) *(u32x4*)(albase + buf * BUFB + aoff[q]) = st.a[q];
+    for (int q = 0; q < PPT; ++q) *(u32x4*)(lds + buf * BUFB + aoff[q]) = st.a[q];
   };
-  auto comp = [&](int buf, const Stage& st) {
-    const char* base = albase + buf * BUFB;
+  auto readb = [&](F8 (&b)[U][MB], int buf) {
+    const char* base = lds + buf * BUFB + boff;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      F8 b[MB];
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < MB; ++j) b[j].u = *(const uint4*)(base + (j * 16 + l16) * ROWB + u * GK * 2 + lg * 16);
+      for (int j = 0; j < MB; ++j) b[u][j].u = *(const uint4*)(base + j * 16 * ROWB + u * GK * 2);
+  };
+  auto mfma = [&](const F8 (&b)[U][MB], const Stage& st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < NR; ++i)
 #pragma unroll
         for (int j = 0; j < MB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.w[u][i].v, b[j].v, acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.w[u][i].v, b[u][j].v, acc[i][j], 0, 0, 0);
   };
-  // Step v of a k-group handles chunk g0 + v from register stage v % NS and
-  // LDS buffer v % 2 (NS is even).  Steps past the group's last chunk load a
-  // clamped, valid chunk and skip the multiply.  An LDS buffer is rewritten
-  // only after the barrier that follows every wave's last read of it.
-  // sched_barrier keeps each phase in program order: the scheduler would
-  // otherwise move W loads ahead of A loads, and the in-order load counter
-  // would then make the LDS store wait for W as well.
-  static_assert(NS % 2 == 0, "stage count must be even");
+  // Chunk c0 + x: W and A pieces in register stage x % NS, A staged in LDS
+  // buffer x % 3 at step x - 2 and read into B[x & 1] at step x - 1.  per
+  // depends on blockIdx only, so every branch and barrier below is uniform
+  // over the workgroup.  Loads past the last chunk are clamped (cache hits,
+  // never multiplied).  Buffer (x + 2) % 3 is rewritten at step x; it was last
+  // read at step x - 2, and two barriers separate the two.  sched_barrier keeps
+  // each phase in program order (the scheduler would otherwise move W loads
+  // ahead of A loads, and the in-order load counter would then make the LDS
+  // store wait for W as well).
   if (per > 0) {
 #pragma unroll
     for (int t = 0; t < NS; ++t) gload(S[t], clampc(t));
     stage(0, S[0]);
+    if (per > 1) stage(1, S[1]);
     __syncthreads();
+    readb(B[0], 0);
+    // full groups first, with no conditions (branches would make the compiler's
+    // wait counts conservative), then the last chunks with them
+    auto step = [&](int x, auto tc, bool next, bool ahead) {
+      constexpr int t = decltype(tc)::value;
+      if (next) readb(B[(t + 1) & 1], (x + 1) % 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(B[t & 1], S[t]);
+      __builtin_amdgcn_sched_barrier(0);
+      gload(S[t], clampc(x + NS));
+      __builtin_amdgcn_sched_barrier(0);
+      if (ahead) stage((x + 2) % 3, S[(t + 2) % NS]);
+      __syncthreads();
+    };
     int v = 0;
-    for (; v + NS <= per; v += NS) {
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        if (g0 + v + t < g1) comp(t & 1, S[t]);
-        __builtin_amdgcn_sched_barrier(0);
-        gload(S[t], clampc(v + t + NS));
-        __builtin_amdgcn_sched_barrier(0);
-        stage((t + 1) & 1, S[(t + 1) % NS]);
-        __syncthreads();
-      }
+    for (; v + NS + 1 < per; v += NS) {
+      step(v + 0, std::integral_constant<int, 0>{}, true, true);
+      step(v + 1, std::integral_constant<int, 1>{}, true, true);
+      step(v + 2, std::integral_constant<int, 2>{}, true, true);
+      step(v + 3, std::integral_constant<int, 3>{}, true, true);
     }
-    // 0 <= per - v < NS steps left, in stages 0.. with step v staged in buffer 0
-    const int left = per - v;
-#pragma unroll
-    for (int t = 0; t < NS - 1; ++t) {
-      if (t < left) {
-        if (g0 + v + t < g1) comp(t & 1, S[t]);
-        if (t + 1 < left) {
-          stage((t + 1) & 1, S[t + 1]);
-          __syncthreads();
-        }
-      }
-    }
-  }
-  if (KG > 1) {
-    // sum the k-groups in group order through LDS (the A buffers are free now)
-    float* red = (float*)lds;
-    __syncthreads();
-    if (kg > 0) {
-      float* dst = red + ((kg - 1) * NG + ng) * TN * TM;
-#pragma unroll
-      for (int i = 0; i < NR; ++i)
-#pragma unroll
-        for (int j = 0; j < MB; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(i * 16 + 4 * lg + r) * TM + j * 16 + l16] = acc[i][j][r];
-    }
-    __syncthreads();
-    if (kg > 0) return;
-#pragma unroll
-    for (int q = 1; q < KG; ++q) {
-      const float* src = red + ((q - 1) * NG + ng) * TN * TM;
-#pragma unroll
-      for (int i = 0; i < NR; ++i)
-#pragma unroll
-        for (int j = 0; j < MB; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] += src[(i * 16 + 4 * lg + r) * TM + j * 16 + l16];
+    for (; v < per; v += NS) {
+      if (v + 0 < per) step(v + 0, std::integral_constant<int, 0>{}, v + 1 < per, v + 2 < per);
+      if (v + 1 < per) step(v + 1, std::integral_constant<int, 1>{}, v + 2 < per, v + 3 < per);
+      if (v + 2 < per) step(v + 2, std::integral_constant<int, 2>{}, v + 3 < per, v + 4 < per);
+      if (v + 3 < per) step(v + 3, std::integral_constant<int, 3>{}, v + 4 < per, v + 5 < per);
     }
   }
   store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
@@ -487,8 +482,6 @@ struct GemmPlan {
   int SK, MB, NR, U, m_tiles, n_tiles;
   bool KW;   // register kernel: the four waves split K
   bool LDS;  // M > 32: A staged in LDS (gemm_lds_kernel)
-  int NS;    // register stages of gemm_lds_kernel
-  int KG;    // k-groups per workgroup of gemm_lds_kernel
   size_t part_bytes;
 };
 
@@ -504,8 +497,6 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
   static const int e_kw = env_int("MEDUSA_GEMM_KW", 1);     // register kernel: waves split K
   static const int e_lds = env_int("MEDUSA_GEMM_LDS", 1);   // M > 32 on gemm_lds_kernel
   static const int e_lnr = env_int("MEDUSA_GEMM_LNR", 0);   // gemm_lds_kernel: W row blocks per wave (1 | 2)
-  static const int e_kg = env_int("MEDUSA_GEMM_KG", 1);     // gemm_lds_kernel: k-groups (1 | 2 | 4)
-  static const int e_ns = env_int("MEDUSA_GEMM_NS", 4);     // gemm_lds_kernel: register stages (2 | 4)
   static const int e_u = env_int("MEDUSA_GEMM_U", 2);       // k-steps per chunk cap (1 | 2 | 4)
   static const int e_waves = env_int("MEDUSA_GEMM_WAVES", 1024);
   static const int e_sk = env_int("MEDUSA_GEMM_SK", 0);     // forced K split (0: from the wave target)
@@ -515,14 +506,11 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
   p.m_tiles = (M + GM - 1) / GM;
   p.LDS = p.MB == 4 && e_lds;
   p.KW = e_kw && !p.LDS;
-  p.NS = e_ns == 2 ? 2 : 4;
-  p.KG = p.LDS ? (e_kg == 4 ? 4 : (e_kg == 2 ? 2 : 1)) : 1;
   const int nsteps = K / GK;
   p.U = nsteps % 4 == 0 ? 4 : (nsteps % 2 == 0 ? 2 : 1);
   while (p.U > e_u && p.U > 1) p.U /= 2;
   if (p.LDS) {
     if (p.U > 2) p.U = 2;
-    if (p.KG == 4) p.U = 1;
     // One workgroup per CU streams best (a second one on some CUs leaves the
     // rest idle at the end): take 128-row tiles when they give >= 160
     // workgroups, else 64-row tiles, and split K across workgroups only when
@@ -530,13 +518,13 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
     const int64_t per_tile = (int64_t)p.m_tiles * batch;
     const int64_t wg2 = (N + 127) / 128 * per_tile, wg1 = (N + 63) / 64 * per_tile;
     p.NR = e_lnr == 1 || e_lnr == 2 ? e_lnr : (wg2 >= 160 ? 2 : 1);
-    const int wg_rows = (4 / p.KG) * p.NR * 16;
+    const int wg_rows = 4 * p.NR * 16;
     p.n_tiles = (N + wg_rows - 1) / wg_rows;
     const int64_t wgs = (int64_t)p.n_tiles * per_tile;
     int sk = e_sk > 0 ? e_sk : (wgs >= 160 ? 1 : (int)(256 / wgs));
     (void)wg1;
     const int nchunks = nsteps / p.U;
-    const int skmax = nchunks / (4 * p.KG) > 0 ? nchunks / (4 * p.KG) : 1;
+    const int skmax = nchunks / 4 > 0 ? nchunks / 4 : 1;
     p.SK = sk < 1 ? 1 : (sk > skmax ? skmax : sk);
   } else {
     p.NR = p.MB == 4 && !e_nr4 ? 2 : 4;
@@ -568,27 +556,16 @@ void gemm_bf16_launch(const GemmPlan& p, int M, int N, int K, const void* A, int
     if (p.KW) GEMM_LAUNCH_KW(MBV, NRV, UV, true); \
     else GEMM_LAUNCH_KW(MBV, NRV, UV, false);     \
   } while (0)
-#define GEMM_LAUNCH_LDS_G(NRV, UV, NSV, KGV)                                                                 \
-  hipLaunchKernelGGL((gemm_lds_kernel<NRV, UV, NSV, KGV>), grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, \
-                     lda, strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
-#define GEMM_LAUNCH_LDS_U(NRV, NSV, KGV)                 \
-  do {                                                   \
-    if (p.U == 2 && KGV < 4) GEMM_LAUNCH_LDS_G(NRV, (KGV < 4 ? 2 : 1), NSV, KGV); \
-    else GEMM_LAUNCH_LDS_G(NRV, 1, NSV, KGV);            \
-  } while (0)
-#define GEMM_LAUNCH_LDS_K(NRV, NSV)                                   \
-  do {                                                                \
-    if (p.KG == 4) GEMM_LAUNCH_LDS_U(NRV, NSV, 4);                    \
-    else if (p.KG == 2) GEMM_LAUNCH_LDS_U(NRV, NSV, 2);               \
-    else GEMM_LAUNCH_LDS_U(NRV, NSV, 1);                              \
-  } while (0)
+#define GEMM_LAUNCH_LDS(NRV, UV, NSV)                                                                      \
+  hipLaunchKernelGGL((gemm_lds_kernel<NRV, UV, NSV>), grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, lda, \
+                     strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
   if (p.LDS) {
     if (p.NR == 1) {
-      if (p.NS == 4) GEMM_LAUNCH_LDS_K(1, 4);
-      else GEMM_LAUNCH_LDS_K(1, 2);
+      if (p.U == 2) GEMM_LAUNCH_LDS(1, 2, 4);
+      else GEMM_LAUNCH_LDS(1, 1, 4);
     } else {
-      if (p.NS == 4) GEMM_LAUNCH_LDS_K(2, 4);
-      else GEMM_LAUNCH_LDS_K(2, 2);
+      if (p.U == 2) GEMM_LAUNCH_LDS(2, 2, 4);
+      else GEMM_LAUNCH_LDS(2, 1, 4);
     }
   } else if (p.MB == 1) {
     if (p.U == 4) GEMM_LAUNCH(1, 4, 4);
@@ -609,9 +586,7 @@ void gemm_bf16_launch(const GemmPlan& p, int M, int N, int K, const void* A, int
   }
 #undef GEMM_LAUNCH
 #undef GEMM_LAUNCH_KW
-#undef GEMM_LAUNCH_LDS_G
-#undef GEMM_LAUNCH_LDS_U
-#undef GEMM_LAUNCH_LDS_K
+#undef GEMM_LAUNCH_LDS
 }
 
 }  // namespace
