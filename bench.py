@@ -9,13 +9,21 @@ reset to 1024 tokens before every step (a device-side copy), so every timed step
 the same workload.
 
 Also measured (same JSON line):
-  roofline       the dominant kernel (the bf16 weight-streaming GEMM) over the GEMM
-                 launches of one step, timed with HIP events, against 8 TB/s
+  roofline       the dominant kernel: gemm_lds_kernel on the gate/up projection of the
+                 64 tree rows (M 64, N 22016, K 4096, SwiGLU epilogue), the largest
+                 single share of the step; average launch time with HIP events over the
+                 32 layers' weights, against 8 TB/s; `traffic` from the committed
+                 rocprofv3 FETCH_SIZE / WRITE_SIZE summary when the kernel source still
+                 matches it.  `step_projections` adds every projection of one step.
   tree_attention the attention kernel alone at batch 8, 32/8 heads, prefix 65536, and
                  at batch 1, prefix 1024, against 8 TB/s
   cpu_baseline   the oracle on the host cores on a bounded sample of the same step
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
+python bench.py --roofline-only      the dominant-kernel launches and a 256 MiB copy
+                                     (counter calibration) only, for rocprofv3 --pmc
+python bench.py --traffic-from FETCH_DIR WRITE_DIR
+                                     turn the two counter runs into the traffic file
 """
 import argparse
 import json
@@ -29,6 +37,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_gate_up_M64_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "speculative_decoding_heads_amd", "csrc", "gemm.hip")
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 
 
 def log(*a):
@@ -44,6 +55,8 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--attn-reps", type=int, default=20)
+    p.add_argument("--roofline-only", action="store_true")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return p.parse_args()
 
 
@@ -71,8 +84,70 @@ def gemm_bytes(M, N, K, out_bytes):
     return N * K * 2 + M * K * 2 + M * N * out_bytes
 
 
+def gate_up_bytes(M, F, d):
+    """Algorithmic bytes of one gate/up launch: W [2F, d] + A [M, d] in, SwiGLU [M, F] out (bf16)."""
+    return 2 * F * d * 2 + M * d * 2 + M * F * 2
+
+
+def source_sha():
+    import hashlib
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per dominant-kernel launch from the committed counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB) per gate/up launch from two rocprofv3 --pmc
+    runs of `bench.py --roofline-only`, each scaled by what the same counter reads for
+    the 256 MiB row copy (gather_rows_kernel, which reads and writes COPY_BYTES) in the
+    same run, written to the traffic file."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = []
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn) as f:
+                rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        gemm = [float(r["Counter_Value"]) for r in rows if "gemm_lds_kernel" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if "gather_rows_kernel" in r["Kernel_Name"]]
+        if not gemm or not copy:
+            raise SystemExit("no %s samples for the GEMM or the copy in %s" % (counter, d))
+        return float(np.median(gemm)), float(np.median(copy))
+
+    g_f, c_f = load(fetch_dir, "FETCH_SIZE")
+    g_w, c_w = load(write_dir, "WRITE_SIZE")
+    ref_kib = COPY_BYTES / 1024.0
+    sf, sw = ref_kib / c_f, ref_kib / c_w
+    fetch_b, write_b = g_f * sf * 1024.0, g_w * sw * 1024.0
+    out = {"kernel": "gemm_lds_kernel gate/up M64 N22016 K4096", "source_sha256": source_sha(),
+           "fetch_kib_raw": g_f, "write_kib_raw": g_w, "copy_fetch_kib_raw": c_f, "copy_write_kib_raw": c_w,
+           "copy_bytes": COPY_BYTES, "fetch_scale": sf, "write_scale": sw,
+           "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+           "bytes_per_launch": round(fetch_b + write_b),
+           "algorithmic_bytes_per_launch": gate_up_bytes(64, 11008, 4096)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
@@ -97,6 +172,21 @@ def main():
     torch.cuda.empty_cache()
     tree = api.Tree(seeded_tree_choices(0))
     B = 1
+    gate_up = make_gate_up(model, cfg, NL, tree.T * B, dev)
+    if args.roofline_only:
+        from speculative_decoding_heads_amd._lib import check, ptr, stream_ptr
+        us = gate_up(2)
+        # calibration: a plain row copy of COPY_BYTES (fp32 rows of 8 KiB) through
+        # the library's gather_rows kernel (row 0 of each one-row sequence)
+        rows = COPY_BYTES // 8192
+        src = torch.ones((rows, 1, 2048), dtype=torch.float32, device=dev)
+        dst = torch.empty((rows, 2048), dtype=torch.float32, device=dev)
+        sel = torch.zeros(rows, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            check(lib().medusa_gather_rows(0, rows, 1, 2048, ptr(src), ptr(sel), ptr(dst), stream_ptr()))
+        torch.cuda.synchronize()
+        print(json.dumps({"gate_up_us": round(us, 3), "copy_bytes": COPY_BYTES}), flush=True)
+        return
     Lmax = args.prefix + 128
     st = State(model, B, Lmax, 64)
     prompt = prompt_tokens(7, B, args.prefix, cfg.vocab)
@@ -161,22 +251,35 @@ def main():
     log("step %.3f ms (wall %.3f ms), %.1f steps/s, mean tokens/step %.2f" % (step_ms, wall_ms, steps_per_s,
                                                                               mean_tokens))
 
-    # ---- dominant kernel: the projection GEMMs of one step at M = 64 rows (plus the heads at M = B)
+    # ---- dominant kernel: the gate/up projection at M = 64 rows, over the 32 layers' weights
     T = tree.T
     M = B * T
     d, F, V, Hq, Dh = cfg.d, cfg.ffn, cfg.vocab, cfg.n_heads, cfg.head_dim
-    gws = torch.empty(max(lib().medusa_gemm_workspace_size(1, M, n, k, 1)
-                          for n, k in [(3 * d, d), (d, d), (2 * F, d), (d, F), (V, d)]) + 256,
-                      dtype=torch.uint8, device=dev)
+    gu_us = gate_up(2)
+    gu_b = gate_up_bytes(M, F, d)
+    gu_gbs = gu_b / (gu_us * 1e-6) / 1e9
+    traffic = read_traffic()
+    log("gate/up GEMM: %.2f us per launch, %.1f GB/s (traffic %s)" % (gu_us, gu_gbs, traffic))
+
+    # ---- every projection of one step as the verify forward issues them
+    from speculative_decoding_heads_amd._lib import check, ptr, stream_ptr
+    need = max([lib().medusa_gemm_workspace_size(1, M, n, k, 1) for n, k in [(3 * d, d), (2 * F, d), (V, d)]] +
+               [lib().medusa_gemm_resid_rmsnorm_workspace_size(1, M, d, k) for k in (d, F)])
+    gws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
     xin = torch_normal((M, F), 1.0, 5, dev, torch.bfloat16)
     outf = torch.empty((M, max(3 * d, V)), dtype=torch.float32, device=dev)
     outb = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
     resid = torch.zeros((M, d), dtype=torch.bfloat16, device=dev)
+    normed = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    gnorm = torch.ones(d, dtype=torch.bfloat16, device=dev)
 
-    def call(A, K, W, N, epi, C, ldc, R=None):
-        from speculative_decoding_heads_amd._lib import check, ptr, stream_ptr
-        check(lib().medusa_gemm(1, M, N, K, ptr(A), K, 0, ptr(W), 0, ptr(C), ldc, 0, 1, epi, ptr(R),
-                                d if R is not None else 0, 0, ptr(gws), gws.numel(), stream_ptr()))
+    def call(A, K, W, N, epi, C, ldc):
+        check(lib().medusa_gemm(1, M, N, K, ptr(A), K, 0, ptr(W), 0, ptr(C), ldc, 0, 1, epi, None, 0, 0, ptr(gws),
+                                gws.numel(), stream_ptr()))
+
+    def call_rn(A, K, W):
+        check(lib().medusa_gemm_resid_rmsnorm(1, M, d, K, ptr(A), K, ptr(W), ptr(resid), ptr(gnorm), 1e-6,
+                                              ptr(normed), ptr(gws), gws.numel(), stream_ptr()))
 
     gemm_launches = []
     for li in range(NL):
@@ -184,9 +287,9 @@ def main():
         wqkv, wgu, wo, wd = lw[0], lw[1], lw[4], lw[5]
         gemm_launches += [
             (lambda w=wqkv: call(xin, d, w, 3 * d, EPI_F32, outf, 3 * d), gemm_bytes(M, 3 * d, d, 4)),
-            (lambda w=wo: call(xin, d, w, d, EPI_RESID, resid, d, resid), gemm_bytes(M, d, d, 4)),
-            (lambda w=wgu: call(xin, d, w, 2 * F, EPI_SWIGLU, outb, F), gemm_bytes(M, 2 * F, d, 2)),
-            (lambda w=wd: call(xin, F, w, d, EPI_RESID, resid, d, resid), gemm_bytes(M, d, F, 4)),
+            (lambda w=wo: call_rn(xin, d, w), gemm_bytes(M, d, d, 2) + 2 * M * d * 2),
+            (lambda w=wgu: call(xin, d, w, 2 * F, EPI_SWIGLU, outb, F), gate_up_bytes(M, F, d)),
+            (lambda w=wd: call_rn(xin, F, w), gemm_bytes(M, d, F, 2) + 2 * M * d * 2),
         ]
     gemm_launches.append((lambda: call(xin, d, model.lm_head, V, EPI_F32, outf, V), gemm_bytes(M, V, d, 4)))
     for f, _ in gemm_launches:
@@ -198,7 +301,7 @@ def main():
     gemm_ms = tg.ms()
     gemm_b = sum(b for _, b in gemm_launches)
     gemm_gbs = gemm_b / (gemm_ms * 1e-3) / 1e9
-    log("projection GEMMs of one step: %.3f ms, %.1f GB/s" % (gemm_ms, gemm_gbs))
+    log("projections of one step: %.3f ms, %.1f GB/s" % (gemm_ms, gemm_gbs))
 
     # ---- tree attention alone
     def attn_case(Bc, L, reps):
@@ -260,11 +363,14 @@ def main():
         "accepted_tok_per_s": round(steps_per_s * mean_tokens, 2),
         "wall_ms_per_step": round(wall_ms, 4),
         "launch": launch,
-        "roofline": {"kernel": "gemm_bf16_kernel (+ split-K reduce): the projection GEMMs of one step at M=64",
-                     "bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gemm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_step": gemm_b, "ms_per_step": round(gemm_ms, 4),
-                     "launches": len(gemm_launches)},
+        "roofline": {"kernel": "gemm_lds_kernel<2,2,4>: gate/up projection, M 64, N 22016, K 4096, SwiGLU",
+                     "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},
+        "step_projections": {"kernels": "gemm_lds_kernel + resid_rmsnorm_kernel: every projection of one step",
+                             "achieved": round(gemm_gbs, 1), "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
+                             "bytes_per_step": gemm_b, "ms_per_step": round(gemm_ms, 4),
+                             "calls": len(gemm_launches)},
         "tree_attention": {
             "B8_L65536": {"us": round(a64_ms * 1e3, 2), "achieved": round(a64_gbs, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(a64_gbs / HBM_PEAK_GBS, 4), "bytes": a64_b},
@@ -273,6 +379,36 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def make_gate_up(model, cfg, NL, M, dev):
+    """Returns run(rounds): the gate/up projection launched over the NL layers' weights
+    `rounds` times after one warm-up round; the average microseconds per launch (HIP
+    events on the stream the library launches on)."""
+    import torch
+    from speculative_decoding_heads_amd._lib import EPI_SWIGLU, check, lib, ptr, stream_ptr
+    from workloads import torch_normal
+    d, F = cfg.d, cfg.ffn
+    A = torch_normal((M, d), 1.0, 5, dev, torch.bfloat16)
+    out = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, lib().medusa_gemm_workspace_size(1, M, 2 * F, d, 1)), dtype=torch.uint8, device=dev)
+    weights = [model.keep[li * 6 + 1] for li in range(NL)]
+
+    def launch(w):
+        check(lib().medusa_gemm(1, M, 2 * F, d, ptr(A), d, 0, ptr(w), 0, ptr(out), F, 0, 1, EPI_SWIGLU, None, 0, 0,
+                                ptr(ws), ws.numel(), stream_ptr()))
+
+    def run(rounds):
+        for w in weights:
+            launch(w)
+        torch.cuda.synchronize()
+        with Timer() as t:
+            for _ in range(rounds):
+                for w in weights:
+                    launch(w)
+        return t.ms() * 1e3 / (rounds * len(weights))
+
+    return run
 
 
 def cpu_baseline(params, heads, sample_layers, model, cfg, tree, prompt, prefix, dev):

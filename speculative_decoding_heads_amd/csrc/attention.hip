@@ -20,6 +20,8 @@
 //  * attn_stream (attn_stream.hip) -- bf16, head size 64 or 128, the
 //    streaming MFMA kernel; with KV splits it writes fp32 partials that
 //    attn_combine (below) merges.
+#include <stdlib.h>
+
 #include "attn_stream.h"
 #include "common.h"
 
@@ -100,32 +102,47 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
   }
 }
 
-// grid (R, Hkv, B), block DH threads: merge the split partials of one query row.
+constexpr int ATTN_MAX_SPLITS = 64;
+
+// grid (R, Hkv, B), block Dh threads: merge the split partials of one query row.
+// The split maxima and sums go through shared memory in one round trip, then
+// each thread adds its dimension over the splits with independent loads.
 template <typename T>
-__global__ void attn_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int Tn, int Hq,
-                                    int Hkv, int Dh, int n_splits, T* __restrict__ out) {
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ ws_o,
+                                                           const float* __restrict__ ws_ml, int Tn, int Hq, int Hkv,
+                                                           int Dh, int n_splits, T* __restrict__ out) {
+  __shared__ float sm[ATTN_MAX_SPLITS], sl[ATTN_MAX_SPLITS];
   const int r = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int R = Tn * G;
   const size_t slab = (size_t)b * Hkv + kvh;
-  float mt = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mt = fmaxf(mt, ws_ml[((slab * n_splits + s) * R + r) * 2]);
-  float lt = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const size_t pr = (slab * n_splits + s) * R + r;
-    const float ms = ws_ml[pr * 2];
-    if (ms != -INFINITY) lt += ws_ml[pr * 2 + 1] * __builtin_amdgcn_exp2f(ms - mt);
+  const size_t base = slab * n_splits * (size_t)R + r;  // partial row of split s: base + s * R
+  for (int s = threadIdx.x; s < n_splits; s += blockDim.x) {
+    sm[s] = ws_ml[(base + (size_t)s * R) * 2];
+    sl[s] = ws_ml[(base + (size_t)s * R) * 2 + 1];
   }
+  __syncthreads();
+  float mt = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mt = fmaxf(mt, sm[s]);
+  float lt = 0.f;
+  for (int s = 0; s < n_splits; ++s)
+    if (sm[s] != -INFINITY) lt += sl[s] * __builtin_amdgcn_exp2f(sm[s] - mt);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const int node = r / G, g = r % G;
   const size_t ooff = (((size_t)b * Tn + node) * Hq + (size_t)kvh * G + g) * Dh;
   for (int d = threadIdx.x; d < Dh; d += blockDim.x) {
     float acc = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const size_t pr = (slab * n_splits + s) * R + r;
-      const float ms = ws_ml[pr * 2];
-      if (ms != -INFINITY) acc += ws_o[pr * Dh + d] * __builtin_amdgcn_exp2f(ms - mt);
+    int s = 0;
+    for (; s + 4 <= n_splits; s += 4) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = ws_o[(base + (size_t)(s + u) * R) * Dh + d];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (sm[s + u] != -INFINITY) acc += v[u] * __builtin_amdgcn_exp2f(sm[s + u] - mt);
     }
+    for (; s < n_splits; ++s)
+      if (sm[s] != -INFINITY) acc += ws_o[(base + (size_t)s * R) * Dh + d] * __builtin_amdgcn_exp2f(sm[s] - mt);
     Elem<T>::store(out, ooff + d, acc * inv);
   }
 }
@@ -144,8 +161,15 @@ MfmaPlan mfma_plan(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint) {
   const int64_t tiles = (L_hint + ATTN_KT - 1) / ATTN_KT;
   const int64_t units = (int64_t)B * Hkv * p.n_rchunks;
   // aim at ~8 waves per CU (256 CUs), each split at least 2 tiles
+  // (MEDUSA_ATTN_MIN_TILES overrides the 2 for tuning runs)
+  static const int min_tiles = [] {
+    const char* e = getenv("MEDUSA_ATTN_MIN_TILES");
+    const int v = e ? atoi(e) : 2;
+    return v >= 1 ? v : 2;
+  }();
   int64_t s = (2048 / p.nw + units - 1) / units;
-  const int64_t smax = (tiles + 1) / 2;
+  int64_t smax = (tiles + min_tiles - 1) / min_tiles;
+  if (smax > ATTN_MAX_SPLITS) smax = ATTN_MAX_SPLITS;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
   p.n_splits = (int)s;

@@ -343,9 +343,10 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
 
 }  // namespace
 
-// Waves per workgroup: one per 32-row block of the rows sharing a KV head, up
-// to 8 (R <= 64 -> 2, R <= 128 -> 4, else 8), always with two register tiles in
-// flight.  MEDUSA_ATTN_WAVES = 2 | 4 | 8 forces a width for tuning runs.
+// Waves per workgroup: one per 32-row block of the rows sharing a KV head, at
+// least 2 and at most 8 (R <= 64 -> 2, R <= 128 -> 4, else 8), always with two
+// register tiles in flight.  MEDUSA_ATTN_WAVES = 2 | 4 | 8 forces a width for
+// tuning runs.
 int attn_stream_waves(int R) {
   static const int forced = [] {
     const char* e = getenv("MEDUSA_ATTN_WAVES");

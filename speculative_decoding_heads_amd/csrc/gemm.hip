@@ -642,67 +642,82 @@ extern "C" int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_
 // ---------------------------------------------------------------------------
 namespace {
 
-// One 256-thread block per row; each thread holds NV vectors of 8 columns.
+// One 512-thread block per row; each thread holds NV vectors of 8 columns.
 // SK > 0: acc = sum_s part[s][m][:] in split order, x[m,:] = bf16(x[m,:] + acc)
 // is stored; SK == 0: x is only read.  Then y[m,:] = bf16(x[m,:] * inv * g)
 // with inv = 1 / sqrt(mean(x[m,:]^2) + eps) taken over the stored bf16 x.
+// Every global read of a row (x, the partials, g) is issued before the first
+// use, so a row costs one memory round trip plus the block reduction.
+constexpr int RN_THREADS = 512;
 template <int NV>
-__global__ __launch_bounds__(256) void resid_rmsnorm_kernel(int M, int N, int SK, const float* __restrict__ part,
-                                                            bf16_t* __restrict__ x, const bf16_t* __restrict__ g,
-                                                            float eps, bf16_t* __restrict__ y) {
+__global__ __launch_bounds__(RN_THREADS) void resid_rmsnorm_kernel(int M, int N, int SK,
+                                                                   const float* __restrict__ part,
+                                                                   bf16_t* __restrict__ x,
+                                                                   const bf16_t* __restrict__ g, float eps,
+                                                                   bf16_t* __restrict__ y) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const int m = blockIdx.x, tid = threadIdx.x;
   bf16_t* xr = x + (size_t)m * N;
+  u32x4 xraw[NV], graw[NV];
   float v[NV][8];
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int n = (q * RN_THREADS + tid) * 8;
+    if (n < N) {
+      xraw[q] = *(const u32x4*)(xr + n);
+      graw[q] = *(const u32x4*)(g + n);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int n = (q * RN_THREADS + tid) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[q][i] = 0.f;
+    if (n >= N) continue;
+    for (int sp = 0; sp < SK; ++sp) {
+      const float4* pp = (const float4*)(part + ((size_t)sp * M + m) * N + n);
+      const float4 a = pp[0], b = pp[1];
+      v[q][0] += a.x; v[q][1] += a.y; v[q][2] += a.z; v[q][3] += a.w;
+      v[q][4] += b.x; v[q][5] += b.y; v[q][6] += b.z; v[q][7] += b.w;
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int q = 0; q < NV; ++q) {
-    const int n = (q * 256 + tid) * 8;
+    const int n = (q * RN_THREADS + tid) * 8;
     if (n >= N) continue;
-    const u32x4 raw = *(const u32x4*)(xr + n);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[q][2 * i] = __uint_as_float(raw[i] << 16);
-      v[q][2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
-    }
-    if (SK > 0) {
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-      for (int sp = 0; sp < SK; ++sp) {
-        const float4* pp = (const float4*)(part + ((size_t)sp * M + m) * N + n);
-        const float4 a = pp[0], b = pp[1];
-        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-      }
-      u32x4 out;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16_t lo = f32_to_bf16(v[q][2 * i] + acc[2 * i]);
-        const bf16_t hi = f32_to_bf16(v[q][2 * i + 1] + acc[2 * i + 1]);
-        v[q][2 * i] = bf16_to_f32(lo);
-        v[q][2 * i + 1] = bf16_to_f32(hi);
-        out[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-      }
-      *(u32x4*)(xr + n) = out;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += v[q][i] * v[q][i];
-  }
-  __shared__ float red[4];
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
-#pragma unroll
-  for (int q = 0; q < NV; ++q) {
-    const int n = (q * 256 + tid) * 8;
-    if (n >= N) continue;
-    const u32x4 graw = *(const u32x4*)(g + n);
     u32x4 out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float g0 = __uint_as_float(graw[i] << 16), g1 = __uint_as_float(graw[i] & 0xffff0000u);
+      float lo = __uint_as_float(xraw[q][i] << 16), hi = __uint_as_float(xraw[q][i] & 0xffff0000u);
+      if (SK > 0) {
+        const bf16_t blo = f32_to_bf16(lo + v[q][2 * i]), bhi = f32_to_bf16(hi + v[q][2 * i + 1]);
+        lo = bf16_to_f32(blo);
+        hi = bf16_to_f32(bhi);
+        out[i] = (uint32_t)blo | ((uint32_t)bhi << 16);
+      }
+      v[q][2 * i] = lo;
+      v[q][2 * i + 1] = hi;
+      ss += lo * lo + hi * hi;
+    }
+    if (SK > 0) *(u32x4*)(xr + n) = out;
+  }
+  __shared__ float red[RN_THREADS / 64];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < RN_THREADS / 64; ++i) tot += red[i];
+  const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+#pragma unroll
+  for (int q = 0; q < NV; ++q) {
+    const int n = (q * RN_THREADS + tid) * 8;
+    if (n >= N) continue;
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g0 = __uint_as_float(graw[q][i] << 16), g1 = __uint_as_float(graw[q][i] & 0xffff0000u);
       out[i] = (uint32_t)f32_to_bf16(v[q][2 * i] * inv * g0) | ((uint32_t)f32_to_bf16(v[q][2 * i + 1] * inv * g1) << 16);
     }
     *(u32x4*)(y + (size_t)m * N + n) = out;
@@ -718,13 +733,11 @@ int resid_rmsnorm_bf16(int M, int N, int SK, const float* part, bf16_t* x, const
                        hipStream_t stream) {
   MEDUSA_REQUIRE(N % 8 == 0 && N <= 8192, MEDUSA_ERR_UNSUPPORTED, "rmsnorm bf16: N=%d (need N %% 8 == 0, <= 8192)", N);
   if (M == 0) return MEDUSA_OK;
-  const int nv = (N + 2047) / 2048;
+  const int nv = (N + RN_THREADS * 8 - 1) / (RN_THREADS * 8);
   if (nv == 1)
-    hipLaunchKernelGGL(resid_rmsnorm_kernel<1>, dim3(M), dim3(256), 0, stream, M, N, SK, part, x, g, eps, y);
-  else if (nv == 2)
-    hipLaunchKernelGGL(resid_rmsnorm_kernel<2>, dim3(M), dim3(256), 0, stream, M, N, SK, part, x, g, eps, y);
+    hipLaunchKernelGGL(resid_rmsnorm_kernel<1>, dim3(M), dim3(RN_THREADS), 0, stream, M, N, SK, part, x, g, eps, y);
   else
-    hipLaunchKernelGGL(resid_rmsnorm_kernel<4>, dim3(M), dim3(256), 0, stream, M, N, SK, part, x, g, eps, y);
+    hipLaunchKernelGGL(resid_rmsnorm_kernel<2>, dim3(M), dim3(RN_THREADS), 0, stream, M, N, SK, part, x, g, eps, y);
   return check_launch("resid_rmsnorm");
 }
 
