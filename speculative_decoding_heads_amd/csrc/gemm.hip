@@ -45,7 +45,17 @@ struct EpiArgs {
   int64_t lda;
   int K;
   int part_only;  // bf16 kernels: always leave fp32 partials (a fused consumer reduces them)
+  // EPI_QKV_ROPE (gemm_lds_kernel with NR == 1, SK == 1): rotary embedding and
+  // the q / K / V split of a fused [(Hq + 2 Hkv) * Dh, d] projection
+  const int32_t* pos;
+  const float* cos_t;
+  const float* sin_t;
+  int max_pos, T, Hq, Hkv, Dh;
+  bf16_t *q_out, *k_out, *v_out;
 };
+
+// Internal epilogue mode (not in the public enum): see EpiArgs.
+constexpr int EPI_QKV_ROPE = 100;
 
 // Apply the epilogue to a pair-capable element set: value v at (m, n).  For
 // SWIGLU the caller passes gate (n even) and up (n+1) together.
@@ -172,6 +182,59 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[NR][MB], int n0, i
           if (nb + r < N) epi_store<bf16_t>(eb, m, nb + r, acc[i][j][r]);
       }
     }
+}
+
+// Rotary embedding + q / K / V split for a wave's 16 x 64 tile of the fused
+// projection (tile mapping of EPI_QKV_ROPE in gemm_lds_kernel).  The partner
+// tile (wave w ^ 1) is exchanged through LDS; every wave of the workgroup
+// calls this (it holds two barriers).  Rotate-half: for i < Dh/2,
+// y[i] = x[i] cos - x[i + Dh/2] sin, y[i + Dh/2] = x[i + Dh/2] cos + x[i] sin,
+// at the row's position (clamped to [0, max_pos)); V rows are stored as they are.
+__device__ __forceinline__ void rope_epilogue(const f32x4 (&acc)[1][4], char* lds, int w, int n0, int m0, int M,
+                                              const EpiArgs& e, int l16, int lg) {
+  float* xs = (float*)lds;  // [4 waves][16 rows][64 columns]
+  __syncthreads();          // every wave is done with the A buffers
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) xs[(w * 16 + 4 * lg + r) * 64 + j * 16 + l16] = acc[0][j][r];
+  __syncthreads();
+  const int Dh = e.Dh, half = Dh / 2;
+  const int hd = n0 / Dh, within = n0 % Dh;
+  const int hf = within >= half;                     // second half of the head
+  const int i0 = (hf ? within - half : within) + 4 * lg;  // first of this lane's 4 dims (in the half)
+  const int partner = w ^ 1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + j * 16 + l16;
+    if (m >= M) continue;
+    const int b = m / e.T, t = m % e.T;
+    float y[4];
+    bf16_t* dst;
+    if (hd < e.Hq + e.Hkv) {
+      int p = e.pos[m];
+      p = p < 0 ? 0 : (p >= e.max_pos ? e.max_pos - 1 : p);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float own = acc[0][j][r];
+        const float par = xs[(partner * 16 + 4 * lg + r) * 64 + j * 16 + l16];
+        const float c = e.cos_t[(size_t)p * half + i0 + r], sn = e.sin_t[(size_t)p * half + i0 + r];
+        // first half: own = x[i], par = x[i + half]; second half: the reverse
+        y[r] = hf ? own * c + par * sn : own * c - par * sn;
+      }
+      const int dim = hf * half + i0;
+      dst = hd < e.Hq ? e.q_out + (((size_t)b * e.T + t) * e.Hq + hd) * Dh + dim
+                      : e.k_out + (((size_t)b * e.Hkv + (hd - e.Hq)) * e.T + t) * Dh + dim;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = acc[0][j][r];
+      dst = e.v_out + (((size_t)b * e.Hkv + (hd - e.Hq - e.Hkv)) * e.T + t) * Dh + within + 4 * lg;
+    }
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+    *(uint2*)dst = pk;
+  }
 }
 
 // Each wave owns an (NR*16 W rows) x (MB*16 A rows) output tile.  With KW the
@@ -321,7 +384,8 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
   constexpr int PPT = GM * PPR / GTHR;   // pieces per thread and chunk (= U)
   constexpr int BUFB = GM * ROWB;
   static_assert(NS == 4, "the step sequence below is written for four register stages");
-  __shared__ __align__(16) char lds[3 * BUFB];
+  // three A buffers; the rotary epilogue reuses them for a 4 x 16 x 64 fp32 exchange
+  __shared__ __align__(16) char lds[3 * BUFB > 16384 ? 3 * BUFB : 16384];
   const int bz = blockIdx.z;
   const int nt = blockIdx.x;
   const int mt = blockIdx.y / SK;
@@ -330,7 +394,16 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
   const int l16 = lane & 15, lg = lane >> 4;
   A += bz * sA;
   W += bz * sW;
-  const int n0 = (nt * 4 + w) * TN, m0 = mt * GM;
+  // EPI_QKV_ROPE maps the four 16-row wave tiles to two blocks of the first
+  // half of one head's rows and the same blocks of the second half (waves
+  // w and w ^ 1 hold the two rotary partners of the same dimensions)
+  const bool rope = e.mode == EPI_QKV_ROPE;
+  int n0 = (nt * 4 + w) * TN;
+  if (rope) {
+    const int wg_per_head = e.Dh / 64, hd = nt / wg_per_head, sub = nt % wg_per_head;
+    n0 = hd * e.Dh + (w & 1) * (e.Dh / 2) + (sub * 2 + (w >> 1)) * 16;
+  }
+  const int m0 = mt * GM;
   const int nchunks = (K / GK) / U;
   const int c0 = (int)((int64_t)nchunks * ks / SK), c1 = (int)((int64_t)nchunks * (ks + 1) / SK);
   const int per = c1 - c0;  // chunks of this workgroup (uniform)
@@ -445,6 +518,12 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
       if (v + 1 < per) step(v + 1, std::integral_constant<int, 1>{}, v + 2 < per, v + 3 < per);
       if (v + 2 < per) step(v + 2, std::integral_constant<int, 2>{}, v + 3 < per, v + 4 < per);
       if (v + 3 < per) step(v + 3, std::integral_constant<int, 3>{}, v + 4 < per, v + 5 < per);
+    }
+  }
+  if constexpr (NR == 1) {
+    if (rope) {
+      rope_epilogue(acc, lds, w, n0, m0, M, e, l16, lg);
+      return;
     }
   }
   store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
@@ -739,6 +818,30 @@ int resid_rmsnorm_bf16(int M, int N, int SK, const float* part, bf16_t* x, const
   else
     hipLaunchKernelGGL(resid_rmsnorm_kernel<2>, dim3(M), dim3(RN_THREADS), 0, stream, M, N, SK, part, x, g, eps, y);
   return check_launch("resid_rmsnorm");
+}
+
+}  // namespace medusa
+
+namespace medusa {
+
+// Fused q/K/V projection with rotary embedding (bf16, M > 32, Dh % 64 == 0):
+// qkv = A W^T for W = [Hq q heads; Hkv k heads; Hkv v heads] x Dh rows, then
+// q [B, T, Hq, Dh] and Kt [B, Hkv, T, Dh] rotated at pos[b*T + t], Vt as is.
+// Returns MEDUSA_ERR_UNSUPPORTED (nothing launched) for shapes it does not take.
+int gemm_qkv_rope_bf16(int B, int T, int K, int Hq, int Hkv, int Dh, const bf16_t* A, const bf16_t* W,
+                       const int32_t* pos, const float* cos_t, const float* sin_t, int max_pos, bf16_t* q_out,
+                       bf16_t* k_out, bf16_t* v_out, hipStream_t stream) {
+  const int M = B * T, N = (Hq + 2 * Hkv) * Dh;
+  if (M <= 32 || Dh % 64 || K % GK || K % 8) return MEDUSA_ERR_UNSUPPORTED;
+  GemmPlan p = gemm_plan(M, N, K, 1);
+  if (!p.LDS) return MEDUSA_ERR_UNSUPPORTED;
+  p.NR = 1;
+  p.SK = 1;
+  p.n_tiles = N / 64;
+  EpiArgs e{EPI_QKV_ROPE, nullptr, 0, nullptr, 0, A, K, K, 0, pos, cos_t, sin_t, max_pos, T, Hq, Hkv, Dh,
+            q_out, k_out, v_out};
+  gemm_bf16_launch(p, M, N, K, A, K, 0, W, 0, e, 0, 0, nullptr, 1, stream);
+  return check_launch("gemm qkv rope");
 }
 
 }  // namespace medusa

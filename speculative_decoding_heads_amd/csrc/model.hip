@@ -160,10 +160,19 @@ extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t
     const bool last = l + 1 == m->n_layers;
     char* kt = (char*)Kt + l * side_layer;
     char* vt = (char*)Vt + l * side_layer;
-    CK(medusa_gemm(dt, M, (Hq + 2 * Hkv) * Dh, d, f.xn, d, 0, w.wqkv, 0, f.qkv, (Hq + 2 * Hkv) * Dh, 0, 1,
-                   MEDUSA_EPI_F32, nullptr, 0, 0, f.gws, f.gws_bytes, stream));
-    CK(medusa_rope_split(dt, B, T, Hq, Hkv, Dh, (const float*)f.qkv, pos, m->rope_cos, m->rope_sin, m->rope_max_pos,
-                         f.q, kt, vt, stream));
+    // bf16: the product's epilogue applies the rotary embedding and splits q/K/V
+    const int fused = dt == MEDUSA_BF16
+                          ? gemm_qkv_rope_bf16(B, T, d, Hq, Hkv, Dh, (const bf16_t*)f.xn, (const bf16_t*)w.wqkv, pos,
+                                               m->rope_cos, m->rope_sin, m->rope_max_pos, (bf16_t*)f.q, (bf16_t*)kt,
+                                               (bf16_t*)vt, stream)
+                          : MEDUSA_ERR_UNSUPPORTED;
+    if (fused != MEDUSA_OK && fused != MEDUSA_ERR_UNSUPPORTED) return fused;
+    if (fused == MEDUSA_ERR_UNSUPPORTED) {
+      CK(medusa_gemm(dt, M, (Hq + 2 * Hkv) * Dh, d, f.xn, d, 0, w.wqkv, 0, f.qkv, (Hq + 2 * Hkv) * Dh, 0, 1,
+                     MEDUSA_EPI_F32, nullptr, 0, 0, f.gws, f.gws_bytes, stream));
+      CK(medusa_rope_split(dt, B, T, Hq, Hkv, Dh, (const float*)f.qkv, pos, m->rope_cos, m->rope_sin,
+                           m->rope_max_pos, f.q, kt, vt, stream));
+    }
     CK(tree_attention(dt, B, T, Hq, Hkv, Dh, f.q, Lmax ? (const char*)Kc + l * cache_layer : nullptr,
                       Lmax ? (const char*)Vc + l * cache_layer : nullptr, Lmax, L_hint, seq_len, kt, vt, anc, scale,
                       f.attn, f.aws, f.aws_bytes, stream));

@@ -124,13 +124,11 @@ def test_tiny_fp32_state_after_steps(dev):
     assert_close(to_np(st.Vc)[:, 0, :, :S], cV[:, 0, :, :S], rtol=1e-5, atol=1e-5, what="V cache")
 
 
-def _small_bf16_model(seed):
+def _small_bf16_model(seed, heads_kv_dim=(8, 4, 64)):
     class Cfg:
         n_layers = 2
         d = 512
-        n_heads = 8
-        n_kv_heads = 4
-        head_dim = 64
+        n_heads, n_kv_heads, head_dim = heads_kv_dim
         ffn = 1024
         vocab = 2048
         n_medusa = 4
@@ -139,12 +137,15 @@ def _small_bf16_model(seed):
     return tiny_model(seed, cfg=Cfg, bf16=True), Cfg
 
 
-def test_bf16_forward_vs_oracle(dev):
+# GQA with head size 64 and MHA with head size 128: both take the fused
+# projection + rotary epilogue (64 tree rows x batch 2 = 128 product rows)
+@pytest.mark.parametrize("heads_kv_dim", [(8, 4, 64), (4, 4, 128)])
+def test_bf16_forward_vs_oracle(dev, heads_kv_dim):
     import torch
     from speculative_decoding_heads_amd import api
     from speculative_decoding_heads_amd.model import Model
-    say("e2e bf16 forward vs oracle")
-    (params, heads), Cfg = _small_bf16_model(3)
+    say("e2e bf16 forward vs oracle", heads_kv_dim)
+    (params, heads), Cfg = _small_bf16_model(3, heads_kv_dim)
     P, H = _upload(params, heads, torch.bfloat16, dev)
     model = Model(P, H, max_pos=1024)
     tree = api.Tree(PAGE_TREE_CHOICES)
@@ -167,6 +168,7 @@ def test_bf16_forward_vs_oracle(dev):
     assert_close(to_np(logits), rl, rtol=2e-2, atol=1e-2 * max(scale, 1.0), what="logits")
     assert_close(to_np(h), rh, rtol=2e-2, atol=1e-2 * np.abs(rh).max(), what="h")
     assert_close(to_np(Kt), rK, rtol=2e-2, atol=1e-2 * np.abs(rK).max(), what="tree K")
+    assert_close(to_np(Vt), rV, rtol=2e-2, atol=1e-2 * np.abs(rV).max(), what="tree V")
 
 
 @pytest.mark.parametrize("mode", [GREEDY, TYPICAL])
