@@ -225,12 +225,28 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
           vf[ksub][db].u[0] = *(const uint2*)(vrow);
           vf[ksub][db].u[1] = *(const uint2*)(vrow + 8);
         }
-      // S^T (32 keys x 32 queries) = K Q^T
+      // S^T (32 keys x 32 queries) = K Q^T.  With few waves per SIMD, two
+      // interleaved accumulation chains (even / odd k-steps) keep consecutive
+      // MFMAs independent; the 8-wave kernel has other waves to overlap and no
+      // registers to spare.
       f32x16 s;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = 0.f;
+      if constexpr (NW <= 4) {
+        f32x16 s1;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], s, 0, 0, 0);
+        for (int e = 0; e < 16; ++e) s1[e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; kk += 2) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], s, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk + 1].v, qf[kk + 1], s1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] += s1[e];
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], s, 0, 0, 0);
+      }
       // lane holds keys kb*32 + 8j + 4*hh + i (value s[4j+i]) of query lq
       if (need_mask) {
         // one 32-bit validity word for the block's keys, then a bit test per key

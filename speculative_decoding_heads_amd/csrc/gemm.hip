@@ -25,6 +25,7 @@
 #include <stdlib.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "medusa_model.h"
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
   constexpr int PPR = U * GK * 2 / 16;   // 16-byte pieces per A row and chunk
   constexpr int PPT = GM * PPR / GTHR;   // pieces per thread and chunk (= U)
   constexpr int BUFB = GM * ROWB;
-  static_assert(NS == 4, "the step sequence below is written for four register stages");
+  static_assert(NS >= 4 && NS % 2 == 0, "the staging distance needs NS >= 4, even");
   // three A buffers; the rotary epilogue reuses them for a 4 x 16 x 64 fp32 exchange
   __shared__ __align__(16) char lds[3 * BUFB > 16384 ? 3 * BUFB : 16384];
   const int bz = blockIdx.z;
@@ -506,19 +507,20 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
       if (ahead) stage((x + 2) % 3, S[(t + 2) % NS]);
       __syncthreads();
     };
+    // NS steps per round, register stage t static in each (index_sequence unrolling)
+    auto full_round = [&](int v, auto... ts) { (step(v + decltype(ts)::value, ts, true, true), ...); };
+    auto last_round = [&](int v, auto... ts) {
+      ((v + decltype(ts)::value < per ? step(v + decltype(ts)::value, ts, v + decltype(ts)::value + 1 < per,
+                                             v + decltype(ts)::value + 2 < per)
+                                      : void()),
+       ...);
+    };
+    auto seq = [&](auto f, int v, auto is) {
+      [&]<int... I>(std::integer_sequence<int, I...>) { f(v, std::integral_constant<int, I>{}...); }(is);
+    };
     int v = 0;
-    for (; v + NS + 1 < per; v += NS) {
-      step(v + 0, std::integral_constant<int, 0>{}, true, true);
-      step(v + 1, std::integral_constant<int, 1>{}, true, true);
-      step(v + 2, std::integral_constant<int, 2>{}, true, true);
-      step(v + 3, std::integral_constant<int, 3>{}, true, true);
-    }
-    for (; v < per; v += NS) {
-      if (v + 0 < per) step(v + 0, std::integral_constant<int, 0>{}, v + 1 < per, v + 2 < per);
-      if (v + 1 < per) step(v + 1, std::integral_constant<int, 1>{}, v + 2 < per, v + 3 < per);
-      if (v + 2 < per) step(v + 2, std::integral_constant<int, 2>{}, v + 3 < per, v + 4 < per);
-      if (v + 3 < per) step(v + 3, std::integral_constant<int, 3>{}, v + 4 < per, v + 5 < per);
-    }
+    for (; v + NS + 1 < per; v += NS) seq(full_round, v, std::make_integer_sequence<int, NS>{});
+    for (; v < per; v += NS) seq(last_round, v, std::make_integer_sequence<int, NS>{});
   }
   if constexpr (NR == 1) {
     if (rope) {
@@ -589,7 +591,8 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
   p.U = nsteps % 4 == 0 ? 4 : (nsteps % 2 == 0 ? 2 : 1);
   while (p.U > e_u && p.U > 1) p.U /= 2;
   if (p.LDS) {
-    if (p.U > 2) p.U = 2;
+    // two k-steps per chunk (four measured slower: more registers, same bytes in flight)
+    p.U = nsteps % 2 == 0 ? 2 : 1;
     // One workgroup per CU streams best (a second one on some CUs leaves the
     // rest idle at the end): take 128-row tiles when they give >= 160
     // workgroups, else 64-row tiles, and split K across workgroups only when

@@ -44,6 +44,8 @@ def _run(dev, choices, B, Hq, Hkv, Dh, L, Lmax, dtype_name, seed, ragged=False, 
     (PAGE_TREE_CHOICES, 1, 64, 8, 130, 192, False),      # G = 8: 512 rows -> two row chunks
     ([], 2, 32, 8, 777, 800, True),                      # T = 1 decode
     (PAGE_TREE_CHOICES, 2, 8, 8, 0, 64, False),          # no prefix at all
+    (PAGE_TREE_CHOICES, 2, 8, 4, 700, 768, True),        # G = 2: 128 rows -> 4-wave workgroups
+    (seeded_tree_choices(0), 1, 32, 32, 1024, 1088, False),  # MHA 64 rows -> 2-wave workgroups (7B shape)
 ])
 def test_bf16_mfma_parity(dev, choices, B, Hq, Hkv, L, Lmax, ragged):
     got, ref = _run(dev, choices, B, Hq, Hkv, 128, L, Lmax, "bf16", seed=L + B, ragged=ragged)
