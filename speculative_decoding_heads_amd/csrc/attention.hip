@@ -155,8 +155,9 @@ struct MfmaPlan {
 MfmaPlan mfma_plan(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint) {
   MfmaPlan p;
   const int R = T * (Hq / Hkv);
-  p.nw = attn_stream_waves(R);
-  const int rows_wg = 32 * p.nw;
+  p.nw = attn_stream_waves();
+  const int nw = p.nw;
+  const int rows_wg = 32 * nw;
   p.n_rchunks = (R + rows_wg - 1) / rows_wg;
   const int64_t tiles = (L_hint + ATTN_KT - 1) / ATTN_KT;
   const int64_t units = (int64_t)B * Hkv * p.n_rchunks;
@@ -167,7 +168,7 @@ MfmaPlan mfma_plan(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint) {
     const int v = e ? atoi(e) : 2;
     return v >= 1 ? v : 2;
   }();
-  int64_t s = (2048 / p.nw + units - 1) / units;
+  int64_t s = (2048 / nw + units - 1) / units;
   int64_t smax = (tiles + min_tiles - 1) / min_tiles;
   if (smax > ATTN_MAX_SPLITS) smax = ATTN_MAX_SPLITS;
   if (s > smax) s = smax;

@@ -5,15 +5,13 @@
 // Medusa", section 一.2: a node only sees its predecessors; section 二.3: the
 // prefix stays visible) times V.
 //
-// One workgroup of NW <= 8 waves per (sequence, KV head, chunk of <= 32*NW
-// query rows, KV split).  The T*G query rows sharing a KV head (G = Hq/Hkv) are all served
-// by a single pass over that head's keys, so K/V bytes are read from HBM once
-// per KV head no matter how many query heads share them.  Wave w owns the
-// 32-row block w:
-//   * 64-key K and V tiles go global -> registers -> LDS, double-buffered in
-//     LDS with a second tile in flight in registers (two tiles of compute hide
-//     each load); V is transposed on the way in so the P.V operand reads are
-//     contiguous;
+// One workgroup of NW waves per (sequence, KV head, chunk of query rows, KV
+// split).  The T*G query rows sharing a KV head (G = Hq/Hkv) are all served by
+// a single pass over that head's keys, so K/V bytes are read from HBM once per
+// KV head no matter how many query heads share them.  Wave w owns the
+// 32-row block w (waves past the rows still help stream the tiles in):
+//   * 64-key K and V tiles stream straight from HBM into LDS (16-byte direct
+//     loads, no register staging), NBUF tiles deep, one barrier per tile;
 //   * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 (fp32
 //     accumulation), Q fragments held in registers for the whole pass;
 //   * online softmax in the log2 domain per 32-key block; O and the row sum
@@ -46,37 +44,81 @@ __device__ __forceinline__ bf16x8 pack8(const float* p) {
   return r;
 }
 
-__device__ __forceinline__ uint4 sel0(bool ok, uint4 v) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+// max / sum of a value and the one held by lane l ^ 32 (gfx950
+// v_permlane32_swap: the two halves of the wave trade places without a trip
+// through LDS, unlike a ds_bpermute shuffle)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DH>
-struct StreamSmem {
-  static constexpr int KP = DH + 8;  // K row pitch (elements): rows land on different banks
-  static constexpr int VP = KT + 4;  // V^T row pitch (elements)
-  bf16_t k[2][KT * KP];
-  bf16_t v[2][DH * VP];
-};
+// One 16-byte direct load per lane into LDS (gfx950 global_load_lds_dwordx4):
+// lane l reads base + off and writes LDS at lds + 16 * l (M0 holds the
+// wave-uniform LDS address, the SGPR pair the global base).  Written as inline
+// assembly: the compiler's own bookkeeping of these loads waits for all of
+// them before any LDS read, which would serialise the tile pipeline; the
+// kernel waits for them itself (s_waitcnt vmcnt + barrier).  One wait state
+// separates the M0 write from the load (the hazard the compiler's scheduler
+// would otherwise cover).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
 
-// DH head size; NW waves per workgroup (32 query rows each); PF tiles held in
-// registers ahead of the LDS tile being computed (1 or 2).
-template <int DH, int NW, int PF>
-__global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
+// LDS chunk permutation: 16-byte chunk c of key row k sits in slot c ^ swz(k)
+template <int DH>
+__device__ __forceinline__ int swz(int k) {
+  if constexpr (DH == 128) return ((k & 3) << 2) | ((k >> 2) & 3);
+  else return (k >> 1) & 7;
+}
+
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Tiles keep the cache layout in LDS (one 64-key tile of K, one of V, each
+// DH*2 bytes a row; the NBUF K tiles first, then the NBUF V tiles), with the
+// 16-byte chunks of a row permuted by swz so that the fragment reads fall in
+// distinct banks.  K fragments are ds_read_b128 of one key row; the V^T operand
+// of the P.V product is read with the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16): four lanes reading 32 contiguous bytes of one key row
+// give each of 16 lanes four keys of one dimension.  Every lane's LDS read
+// offsets are computed once; tiles that need no mask (all but a ragged last
+// prefix tile and the tree tile, which come last) run with the buffer index a
+// compile-time constant, so each read is one instruction with an immediate
+// offset.  Rows past the valid keys of a tile load a copy of its first row
+// (finite values that the mask then removes).
+template <int DH, int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) void attn_lds_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kc, const bf16_t* __restrict__ Vc, int64_t Lmax,
     const int32_t* __restrict__ seq_len, const bf16_t* __restrict__ Kt, const bf16_t* __restrict__ Vt,
     const uint64_t* __restrict__ anc, int Tn, int Hq, int Hkv, int n_rchunks, float scale_log2, int n_splits,
     bf16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  using S = StreamSmem<DH>;
-  constexpr int NTHR = NW * 64;
   constexpr int ROWS_WG = NW * 32;
-  constexpr int KP = S::KP, VP = S::VP;
   constexpr int NKK = DH / 16;           // k-steps of the S^T product
   constexpr int NDB = DH / 32;           // 32-row blocks of O^T
   constexpr int CPR = DH / 8;            // 16-byte chunks per K/V row
-  constexpr int KCH = KT * CPR / NTHR;   // K chunks per thread
-  constexpr int KPT = KT * CPR / NTHR;   // keys per thread in the V transpose (1, 2 or 4)
+  constexpr int ROWB = DH * 2;           // bytes per K/V row in LDS
+  constexpr int TILEB = KT * ROWB;       // bytes of one K (or V) tile
+  constexpr int RPI = 1024 / ROWB;       // rows per 64-lane load instruction
+  constexpr int NI = KT / RPI;           // load instructions per K (or V) tile
+  constexpr int MPH = NI / NW;           // ... of them issued by each wave
+  constexpr int IPW = 2 * MPH;           // load instructions per wave and tile (K and V)
+  static_assert(MPH >= 1 && NI % NW == 0, "tile load split");
+  static_assert(NBUF >= 2 && (NBUF - 2) * IPW <= 63, "wait count range");
+  static_assert(2 * NBUF * TILEB <= 160 * 1024, "LDS size");
   constexpr float RESCALE_SLACK = 8.0f;  // log2 units
-  __shared__ S sm;
+  __shared__ __align__(16) char sm[2 * NBUF * TILEB];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -86,12 +128,11 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
   const int R = Tn * G;
   const int r0 = rchunk * ROWS_WG;
   const int nr = min(ROWS_WG, R - r0);
-  const int nrb = (nr + 31) >> 5;
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int lq = lane & 31;  // query column of the row block / key row of a key block
-  const int hh = lane >> 5;  // lane half
+  const int lq = lane & 31;
+  const int hh = lane >> 5;
 
   int64_t L = seq_len[b];
   if (L > Lmax) L = Lmax;
@@ -103,6 +144,9 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
   const int npre = t_end - t_begin;
   const bool has_tree = split == n_splits - 1;
   const int ntile = npre + (has_tree ? 1 : 0);
+  // tiles 0 .. nfast-1 are whole prefix tiles; the rest (a ragged last prefix
+  // tile, the tree tile) need the mask
+  const int nfast = npre - (npre > 0 && t_end == tiles && (L % KT) != 0 ? 1 : 0);
 
   const size_t slab = (size_t)b * Hkv + kvh;
   const bf16_t* kc = Kc + slab * Lmax * DH;
@@ -111,23 +155,14 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
   const bf16_t* vt = Vt + slab * Tn * DH;
   const uint64_t tmask = Tn >= 64 ? ~0ull : ((1ull << Tn) - 1ull);
 
-  // ---- this wave's row block: query fragments (B operand of S^T), mask word
-  const bool act = __builtin_amdgcn_readfirstlane((int)(w < nrb)) != 0;  // wave-uniform
+  // ---- this wave's row block: query row, node / head in group, mask word
+  const bool act = w * 32 < nr;  // wave-uniform (w is)
   const int qrow = r0 + w * 32 + lq;
   const bool real = act && qrow < R;
   const int qnode = real ? qrow / G : 0;
   const int qg = real ? qrow % G : 0;
   const uint64_t qmask = real ? (anc[qnode] & tmask) : 1ull;
-  bf16x8 qf[NKK];
-  {
-    const bf16_t* qp = q + (((size_t)b * Tn + qnode) * Hq + (size_t)kvh * G + qg) * DH;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      Frag8 f;
-      f.u = sel0(real, *(const uint4*)(qp + kk * 16 + hh * 8));
-      qf[kk] = f.v;
-    }
-  }
+  bf16x8 qf[NKK];  // query fragments (B operand of S^T), loaded after the first tiles'
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -135,133 +170,142 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
 
-  // ---- tile staging
-  struct Stage {
-    uint4 k[KCH];
-    uint4 v[KPT];
-  };
-  Stage R0;
-  [[maybe_unused]] Stage R1;
-  const int vkg = tid / CPR;  // V: group of KPT consecutive keys
-  const int vch = tid % CPR;  // V: 8-dim chunk
-
-  auto load_tile = [&](int it, Stage& st) {
-    const bool tree = it >= npre;
-    const int64_t base = tree ? 0 : (int64_t)(t_begin + it) * KT;
+  // ---- tile loads: instruction j of this wave fills rows (w + NW*j)*RPI ..
+  // of a K tile and the same rows of a V tile; lane row / slot within it
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)sm);
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  int drow[MPH];
+  uint32_t doff[MPH];
+#pragma unroll
+  for (int j = 0; j < MPH; ++j) {
+    drow[j] = (w + NW * j) * RPI + lrow;
+    doff[j] = (uint32_t)(drow[j] * ROWB + ((lslot ^ swz<DH>(drow[j])) * 16));
+  }
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
+    const bool tree = t >= npre;
+    const int64_t base = tree ? 0 : (int64_t)(t_begin + t) * KT;
     const int nvalid = tree ? Tn : (int)min<int64_t>(KT, L - base);
     const bf16_t* ksrc = tree ? kt : kc + base * DH;
     const bf16_t* vsrc = tree ? vt : vc + base * DH;
-    // rows past nvalid read row 0 (in bounds) and are zeroed by a select
+    const uint32_t lk = lds0 + buf * TILEB + w * 1024;
+    if (nvalid >= KT) {
 #pragma unroll
-    for (int e = 0; e < KCH; ++e) {
-      const int c = tid + e * NTHR;
-      const int row = c / CPR, ch = c % CPR;
-      const bool ok = row < nvalid;
-      st.k[e] = sel0(ok, *(const uint4*)(ksrc + (size_t)(ok ? row : 0) * DH + ch * 8));
-    }
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      const int row = vkg * KPT + e;
-      const bool ok = row < nvalid;
-      st.v[e] = sel0(ok, *(const uint4*)(vsrc + (size_t)(ok ? row : 0) * DH + vch * 8));
-    }
-  };
-  auto store_tile = [&](const Stage& st, int buf) {
-#pragma unroll
-    for (int e = 0; e < KCH; ++e) {
-      const int c = tid + e * NTHR;
-      const int row = c / CPR, ch = c % CPR;
-      *(uint4*)(&sm.k[buf][row * KP + ch * 8]) = st.k[e];
-    }
-    // transpose: V^T row (vch*8 + d) gets this thread's KPT consecutive keys
-    const uint32_t* vw = (const uint32_t*)st.v;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      uint32_t h[KPT];
-#pragma unroll
-      for (int e = 0; e < KPT; ++e) {
-        const uint32_t word = vw[e * 4 + (d >> 1)];
-        h[e] = (d & 1) ? (word >> 16) : (word & 0xffffu);
+      for (int j = 0; j < MPH; ++j) {
+        dma16(ksrc, doff[j], lk + NW * 1024 * j);
+        dma16(vsrc, doff[j], lk + NW * 1024 * j + NBUF * TILEB);
       }
-      bf16_t* dst = &sm.v[buf][(vch * 8 + d) * VP + vkg * KPT];
-      if constexpr (KPT == 8) {
-        // V^T rows are 8-byte aligned (pitch 68 elements)
-        *(uint2*)dst = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        *(uint2*)(dst + 4) = make_uint2(h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-      } else if constexpr (KPT == 4) {
-        *(uint2*)dst = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      } else if constexpr (KPT == 2) {
-        *(uint32_t*)dst = h[0] | (h[1] << 16);
-      } else {
-        *dst = (bf16_t)h[0];
+    } else {
+#pragma unroll
+      for (int j = 0; j < MPH; ++j) {
+        const uint32_t off = drow[j] < nvalid ? doff[j] : doff[j] - (uint32_t)(drow[j] * ROWB);
+        dma16(ksrc, off, lk + NW * 1024 * j);
+        dma16(vsrc, off, lk + NW * 1024 * j + NBUF * TILEB);
       }
     }
   };
 
-  auto compute_tile = [&](int it, int buf) {
-    if (!act) return;
-    const bool tree = it >= npre;
-    const int64_t base = tree ? 0 : (int64_t)(t_begin + it) * KT;
-    const int nvalid = tree ? Tn : (int)min<int64_t>(KT, L - base);
-    const bool need_mask = tree || nvalid < KT;
-    const bf16_t* ks = sm.k[buf];
-    const bf16_t* vs = sm.v[buf];
+  // ---- LDS read offsets of this lane, relative to the tile's K (V) buffer:
+  // K fragment kk of key kb*32 + lq at kl[kk] + kb*32*ROWB; V^T (transpose
+  // read) for key block kb, sub-block ksub at vl[rd][db] + (kb*32 + 16*ksub)*ROWB,
+  // where source lane s of 16-lane group g points at key 8*rd + 4*(g>>1) + s/4,
+  // dimension db*32 + 16*(g&1) + 4*(s%4) (vl includes the V region's offset)
+  uint32_t kl[NKK];
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb) {
-      // all LDS fragment reads of the block are issued up front: the K reads
-      // overlap each other, the V reads overlap the S product and the softmax
-      Frag8 kf[NKK];
+  for (int kk = 0; kk < NKK; ++kk) kl[kk] = (uint32_t)(lq * ROWB + (((kk * 2 + hh) ^ swz<DH>(lq)) * 16));
+  uint32_t vl[2][NDB];
+  {
+    const int vg = lane >> 4, vs = lane & 15;
+    const int vkey = 4 * (vg >> 1) + (vs >> 2);
+    const int vdim = 16 * (vg & 1) + 4 * (vs & 3);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kf[kk].u = *(const uint4*)(ks + (kb * 32 + lq) * KP + kk * 16 + hh * 8);
-      union VF {
-        uint2 u[2];
-        bf16x8 v;
-      } vf[2][NDB];
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int key = 8 * rd + vkey;
+        const int dim = db * 32 + vdim;
+        vl[rd][db] = (uint32_t)(NBUF * TILEB + key * ROWB + (((dim >> 3) ^ swz<DH>(key)) * 16) + (dim & 7) * 2);
+      }
+  }
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  union VF {
+    v4i16 h[2];
+    bf16x8 v;
+  };
+
+  // One tile's products and online softmax, as two 32-key units u = 0, 1.
+  // MASKED: apply the key mask (ragged tile or tree tile); UB: the buffer as a
+  // compile-time constant, or -1 to take buf_rt.  The work is ordered so that
+  // the matrix cores and the vector ALU overlap within the wave: unit 1's S
+  // products run while unit 0's exponentials are computed, and unit 0's P.V
+  // products while unit 1's row maxima are (sched_group_barrier interleaves
+  // them one product at a time).  Only the rare rescale of O and the row sum
+  // sits behind a branch, between the two.
+  auto compute = [&](auto MASKED, auto UB, int buf_rt, int it) __attribute__((always_inline)) {
+    constexpr bool MK = decltype(MASKED)::value;
+    constexpr int UBV = decltype(UB)::value;
+    const uint32_t boff = UBV >= 0 ? (uint32_t)(UBV * TILEB) : (uint32_t)(buf_rt * TILEB);
+    const char* smb = sm + boff;
+    bool tree = false;
+    int nvalid = KT;
+    if constexpr (MK) {
+      tree = it >= npre;
+      const int64_t base = tree ? 0 : (int64_t)(t_begin + it) * KT;
+      nvalid = tree ? Tn : (int)min<int64_t>(KT, L - base);
+    }
+    Frag8 kf[NKK];
+    VF vf[2][NDB];
+    auto load_k = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kf[kk].u = *(const uint4*)(smb + kl[kk] + kb * 32 * ROWB);
+    };
+    auto load_v = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
       for (int ksub = 0; ksub < 2; ++ksub)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16_t* vrow = vs + (db * 32 + lq) * VP + kb * 32 + ksub * 16 + 4 * hh;
-          vf[ksub][db].u[0] = *(const uint2*)(vrow);
-          vf[ksub][db].u[1] = *(const uint2*)(vrow + 8);
-        }
-      // S^T (32 keys x 32 queries) = K Q^T.  With few waves per SIMD, two
-      // interleaved accumulation chains (even / odd k-steps) keep consecutive
-      // MFMAs independent; the 8-wave kernel has other waves to overlap and no
-      // registers to spare.
-      f32x16 s;
+        for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-      if constexpr (NW <= 4) {
+          for (int db = 0; db < NDB; ++db)
+            vf[ksub][db].h[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(smb + vl[rd][db] + (kb * 32 + 16 * ksub) * ROWB));
+    };
+    // S^T block: lane holds keys kb*32 + 8j + 4*hh + i (value s[4j+i]) of
+    // query row lq; `split_chain` runs the products as two chains (even and
+    // odd k-steps) when nothing else fills the gaps between them
+    auto qk = [&](f32x16& sr, bool split_chain) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sr[e] = 0.f;
+      if (split_chain) {
         f32x16 s1;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s1[e] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < NKK; kk += 2) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], s, 0, 0, 0);
+          sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], sr, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk + 1].v, qf[kk + 1], s1, 0, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] += s1[e];
+        for (int e = 0; e < 16; ++e) sr[e] += s1[e];
       } else {
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], s, 0, 0, 0);
+        for (int kk = 0; kk < NKK; ++kk) sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], sr, 0, 0, 0);
       }
-      // lane holds keys kb*32 + 8j + 4*hh + i (value s[4j+i]) of query lq
-      if (need_mask) {
-        // one 32-bit validity word for the block's keys, then a bit test per key
+    };
+    // masked keys -> -inf, then the row maximum in log2 units
+    auto rowmax = [&](f32x16& sr, int kb) __attribute__((always_inline)) {
+      if constexpr (MK) {
         const int nv = nvalid - kb * 32;
         const uint32_t kbits = tree ? (uint32_t)(qmask >> (kb * 32))
                                     : (nv >= 32 ? 0xffffffffu : (nv <= 0 ? 0u : ((1u << nv) - 1u)));
         const uint32_t mine = kbits >> (4 * hh);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = ((mine >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[e] : -INFINITY;
+        for (int e = 0; e < 16; ++e) sr[e] = ((mine >> (8 * (e >> 2) + (e & 3))) & 1u) ? sr[e] : -INFINITY;
       }
-      float mx = s[0];
+      float mx = sr[0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mt = mx * scale_log2;
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sr[e]);
+      return halves_max(mx) * scale_log2;
+    };
+    auto rescale = [&](float mt) __attribute__((always_inline)) {
       if (mt > mrun + RESCALE_SLACK) {
         const float alpha = __builtin_amdgcn_exp2f(mrun - mt);
         lrun *= alpha;
@@ -271,64 +315,117 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
           for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
         mrun = mt;
       }
+    };
+    // P^T B operand: k-slot t of lane half hh <-> key 16*ksub + 8*(t/4) + 4*hh + t%4,
+    // the same key order as the transposed V^T fragment
+    auto expo = [&](const f32x16& sr, bf16x8* pb) __attribute__((always_inline)) {
       const float negm = mrun == -INFINITY ? 0.f : -mrun;
       float p[16];
       float ps = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, negm));
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sr[e], scale_log2, negm));
         ps += p[e];
       }
       lrun += ps;
-      // P^T B operand: k-slot t of lane half hh <-> key 16*ksub + 8*(t/4) + 4*hh + t%4
-      const bf16x8 pb0 = pack8(p), pb1 = pack8(p + 8);
+      pb[0] = pack8(p);
+      pb[1] = pack8(p + 8);
+    };
+    auto pv = [&](const bf16x8* pb) __attribute__((always_inline)) {
 #pragma unroll
       for (int ksub = 0; ksub < 2; ++ksub)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ksub][db].v, ksub ? pb1 : pb0, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ksub][db].v, pb[ksub], o[db], 0, 0, 0);
+    };
+
+    f32x16 s0, s1;
+    bf16x8 pb[2];
+    // unit 0 products (nothing to overlap yet), then unit 1's K and unit 0's V
+    load_k(0);
+    qk(s0, true);
+    load_k(1);
+    load_v(0);
+    rescale(rowmax(s0, 0));
+    // unit 1 products || unit 0 exponentials; unit 0 P.V || unit 1 maximum
+    qk(s1, false);
+    expo(s0, pb);
+    pv(pb);
+    const float mt1 = rowmax(s1, 1);
+#pragma unroll
+    for (int i = 0; i < NKK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // vector ALU
     }
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+    load_v(1);
+    rescale(mt1);
+    expo(s1, pb);
+    pv(pb);
   };
 
-  if constexpr (PF == 2) {
-    // tile it in LDS buffer (it & 1), tile it+1 in registers, tile it+2 being
-    // fetched; unrolled by two so the register stages are static
-    if (ntile > 0) {
-      load_tile(0, R0);
-      store_tile(R0, 0);
-    }
-    if (ntile > 1) load_tile(1, R1);
-    __syncthreads();
-    int it = 0;
-    for (; it + 1 < ntile; it += 2) {
-      if (it + 2 < ntile) load_tile(it + 2, R0);
-      compute_tile(it, 0);
-      store_tile(R1, 1);
-      __syncthreads();
-      if (it + 3 < ntile) load_tile(it + 3, R1);
-      compute_tile(it + 1, 1);
-      if (it + 2 < ntile) store_tile(R0, 0);
-      __syncthreads();
-    }
-    if (it < ntile) compute_tile(it, 0);
-  } else {
-    // tile it in LDS buffer (it & 1) while tile it+1 is fetched into registers
-    if (ntile > 0) {
-      load_tile(0, R0);
-      store_tile(R0, 0);
+  // ---- pipeline: tiles 0 .. NBUF-2 in flight before the loop; step it waits
+  // for tile it (this wave's loads, then the barrier for everyone's), refills
+  // the buffer that tile it-1 used (free: every wave has passed the barrier, so
+  // is done with it) with tile it+NBUF-1; then tile it is computed.
+  auto pipeline_step = [&](int it) __attribute__((always_inline)) {
+    // loads issued after tile it's: min(NBUF-2, ntile-1-it) tiles; s_waitcnt
+    // encoding: vmcnt[3:0] and [15:14], expcnt and lgkmcnt left at "no wait"
+    if (ntile - 1 - it >= NBUF - 2) {
+      constexpr int WN = (NBUF - 2) * IPW;
+      __builtin_amdgcn_s_waitcnt((WN & 0xf) | (0x7 << 4) | (0xf << 8) | (((WN >> 4) & 0x3) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
     }
     __syncthreads();
-    for (int it = 0; it < ntile; ++it) {
-      if (it + 1 < ntile) load_tile(it + 1, R0);
-      compute_tile(it, it & 1);
-      if (it + 1 < ntile) store_tile(R0, (it + 1) & 1);
-      __syncthreads();
+    if (it + NBUF - 1 < ntile) issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
+  };
+
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < ntile) issue_tile(t, t);
+  {
+    // rows past R read row 0 of the head (in bounds); their columns of S and
+    // O are never stored, so no select is needed (a select per load makes the
+    // compiler serialise the loads on shared registers)
+    const bf16_t* qp = q + (((size_t)b * Tn + qnode) * Hq + (size_t)kvh * G + qg) * DH;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      Frag8 f;
+      f.u = *(const uint4*)(qp + kk * 16 + hh * 8);
+      qf[kk] = f.v;
     }
+  }
+  // The query loads go out after the first tiles' loads and complete here,
+  // before the tile loop: the compiler counts only its own loads, and its wait
+  // for these, were it placed inside the loop, would also wait for every tile
+  // load issued after them.  The empty asm reads each fragment, so the loads
+  // cannot sink past this point and that wait lands here (it also covers the
+  // prologue tiles, issued just before).
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
+
+  for (int it0 = 0; it0 < nfast; it0 += NBUF) {
+    static_for<NBUF>([&](auto UC) __attribute__((always_inline)) {
+      constexpr int u = decltype(UC)::value;
+      const int it = it0 + u;
+      if (it >= nfast) return;
+      pipeline_step(it);
+      if (act) compute(std::false_type{}, UC, 0, it);
+    });
+  }
+  for (int it = nfast; it < ntile; ++it) {
+    pipeline_step(it);
+    if (act) compute(std::true_type{}, std::integral_constant<int, -1>{}, it % NBUF, it);
   }
 
   // ---- epilogue: O^T lane layout is rows dh = db*32 + 8j + 4*hh + i of query lq
   if (!real) return;
-  const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+  const float ltot = halves_sum(lrun);
   if (n_splits == 1) {
     bf16_t* op = out + (((size_t)b * Tn + qnode) * Hq + (size_t)kvh * G + qg) * DH;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
@@ -336,10 +433,10 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(o[db][4 * j + 0] * inv) | ((uint32_t)f32_to_bf16(o[db][4 * j + 1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16(o[db][4 * j + 2] * inv) | ((uint32_t)f32_to_bf16(o[db][4 * j + 3] * inv) << 16);
-        *(uint2*)(op + db * 32 + 8 * j + 4 * hh) = pk;
+        bf16x4 pk;  // round to nearest even (v_cvt_pk_bf16_f32)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk[i] = (__bf16)(o[db][4 * j + i] * inv);
+        *(bf16x4*)(op + db * 32 + 8 * j + 4 * hh) = pk;
       }
   } else {
     const size_t prow = (slab * n_splits + split) * (size_t)R + qrow;
@@ -359,30 +456,28 @@ __global__ __launch_bounds__(NW * 64) void attn_stream_kernel(
 
 }  // namespace
 
-// Waves per workgroup: one per 32-row block of the rows sharing a KV head, at
-// least 2 and at most 8 (R <= 64 -> 2, R <= 128 -> 4, else 8), always with two
-// register tiles in flight.  MEDUSA_ATTN_WAVES = 2 | 4 | 8 forces a width for
-// tuning runs.
-int attn_stream_waves(int R) {
+// Waves per workgroup: 8 (the waves past the rows of a KV head still stream
+// tiles in, which keeps more loads in flight); MEDUSA_ATTN_WAVES = 2 | 4 | 8
+// forces a width for tuning runs.
+int attn_stream_waves() {
   static const int forced = [] {
     const char* e = getenv("MEDUSA_ATTN_WAVES");
     const int v = e ? atoi(e) : 0;
     return v == 2 || v == 4 || v == 8 ? v : 0;
   }();
-  if (forced) return forced;
-  return R <= 64 ? 2 : (R <= 128 ? 4 : 8);
+  return forced ? forced : 8;
 }
 
-template <int NW, int PF>
-static void launch_v(int Dh, dim3 grid, hipStream_t stream, const bf16_t* q, const bf16_t* Kc, const bf16_t* Vc,
+template <int NW, int NBUF>
+static void launch_d(int Dh, dim3 grid, hipStream_t stream, const bf16_t* q, const bf16_t* Kc, const bf16_t* Vc,
                      int64_t Lmax, const int32_t* seq_len, const bf16_t* Kt, const bf16_t* Vt, const uint64_t* anc,
                      int T, int Hq, int Hkv, int n_rchunks, float scale_log2, int n_splits, bf16_t* out, float* ws_o,
                      float* ws_ml) {
   if (Dh == 128)
-    hipLaunchKernelGGL((attn_stream_kernel<128, NW, PF>), grid, dim3(NW * 64), 0, stream, q, Kc, Vc, Lmax, seq_len,
+    hipLaunchKernelGGL((attn_lds_kernel<128, NW, NBUF>), grid, dim3(NW * 64), 0, stream, q, Kc, Vc, Lmax, seq_len,
                        Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2, n_splits, out, ws_o, ws_ml);
   else
-    hipLaunchKernelGGL((attn_stream_kernel<64, NW, PF>), grid, dim3(NW * 64), 0, stream, q, Kc, Vc, Lmax, seq_len,
+    hipLaunchKernelGGL((attn_lds_kernel<64, NW, NBUF>), grid, dim3(NW * 64), 0, stream, q, Kc, Vc, Lmax, seq_len,
                        Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2, n_splits, out, ws_o, ws_ml);
 }
 
@@ -391,16 +486,30 @@ int launch_attn_stream(int Dh, int nw, dim3 grid, hipStream_t stream, const bf16
                        const uint64_t* anc, int T, int Hq, int Hkv, int n_rchunks, float scale_log2, int n_splits,
                        bf16_t* out, float* ws_o, float* ws_ml) {
   if (Dh != 128 && Dh != 64) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: streaming kernel takes Dh 64 or 128");
-  if (nw == 2)
-    launch_v<2, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
-                   n_splits, out, ws_o, ws_ml);
-  else if (nw == 4)
-    launch_v<4, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
-                   n_splits, out, ws_o, ws_ml);
-  else
-    launch_v<8, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, scale_log2,
-                   n_splits, out, ws_o, ws_ml);
-  return check_launch("tree_attention stream");
+  // Tile depth: three buffers when every workgroup has a compute unit to
+  // itself (deeper prefetch for short per-workgroup runs), else two (half the
+  // LDS).  MEDUSA_ATTN_NBUF = 2 | 3 | 4 forces a depth (tuning runs).
+  static const int forced_nbuf = [] {
+    const char* e = getenv("MEDUSA_ATTN_NBUF");
+    const int v = e ? atoi(e) : 0;
+    return v == 2 || v == 3 || v == 4 ? v : 0;
+  }();
+  const long wgs = (long)grid.x * grid.y * grid.z;
+  const int nbuf = forced_nbuf ? forced_nbuf : (wgs <= 256 ? 3 : 2);
+#define LD(NWV)                                                                                                      \
+  do {                                                                                                               \
+    if (nbuf == 2) launch_d<NWV, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, \
+                                    scale_log2, n_splits, out, ws_o, ws_ml);                                         \
+    else if (nbuf == 4) launch_d<NWV, 4>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv,       \
+                                         n_rchunks, scale_log2, n_splits, out, ws_o, ws_ml);                         \
+    else launch_d<NWV, 3>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks,           \
+                          scale_log2, n_splits, out, ws_o, ws_ml);                                                   \
+  } while (0)
+  if (nw == 2) LD(2);
+  else if (nw == 4) LD(4);
+  else LD(8);
+#undef LD
+  return check_launch("tree_attention");
 }
 
 }  // namespace medusa

@@ -41,11 +41,13 @@ def _run(dev, choices, B, Hq, Hkv, Dh, L, Lmax, dtype_name, seed, ragged=False, 
     (PAGE_TREE_CHOICES, 2, 8, 2, 300, 320, True),       # ragged, several tiles, partial last tile
     (seeded_tree_choices(0), 1, 32, 8, 1024, 1024, False),  # the 1k-prefix kernel shape
     (TWO_HEAD_CHOICES, 3, 4, 4, 200, 256, True),         # MHA, small tree
-    (PAGE_TREE_CHOICES, 1, 64, 8, 130, 192, False),      # G = 8: 512 rows -> two row chunks
+    (PAGE_TREE_CHOICES, 1, 64, 8, 130, 192, False),      # G = 8: 512 rows -> two 256-row chunks
     ([], 2, 32, 8, 777, 800, True),                      # T = 1 decode
     (PAGE_TREE_CHOICES, 2, 8, 8, 0, 64, False),          # no prefix at all
-    (PAGE_TREE_CHOICES, 2, 8, 4, 700, 768, True),        # G = 2: 128 rows -> 4-wave workgroups
-    (seeded_tree_choices(0), 1, 32, 32, 1024, 1088, False),  # MHA 64 rows -> 2-wave workgroups (7B shape)
+    (PAGE_TREE_CHOICES, 2, 8, 4, 700, 768, True),        # G = 2: 128 rows, half the waves without rows
+    (TWO_HEAD_CHOICES, 2, 32, 2, 333, 384, True),        # G = 16: 144 rows -> a partial 32-row block
+    (chain_choices(11), 1, 32, 2, 2000, 2048, False),    # G = 16: 192 rows, a chain tree
+    (seeded_tree_choices(0), 1, 32, 32, 1024, 1088, False),  # MHA 64 rows (7B shape)
 ])
 def test_bf16_mfma_parity(dev, choices, B, Hq, Hkv, L, Lmax, ragged):
     got, ref = _run(dev, choices, B, Hq, Hkv, 128, L, Lmax, "bf16", seed=L + B, ragged=ragged)
