@@ -232,159 +232,148 @@ __global__ __launch_bounds__(NW * 64) void attn_lds_kernel(
     bf16x8 v;
   };
 
-  // One tile's products and online softmax, as two 32-key units u = 0, 1.
-  // MASKED: apply the key mask (ragged tile or tree tile); UB: the buffer as a
-  // compile-time constant, or -1 to take buf_rt.  The work is ordered so that
-  // the matrix cores and the vector ALU overlap within the wave: unit 1's S
-  // products run while unit 0's exponentials are computed, and unit 0's P.V
-  // products while unit 1's row maxima are (sched_group_barrier interleaves
-  // them one product at a time).  Only the rare rescale of O and the row sum
-  // sits behind a branch, between the two.
-  auto compute = [&](auto MASKED, auto UB, int buf_rt, int it) __attribute__((always_inline)) {
-    constexpr bool MK = decltype(MASKED)::value;
+  // ---- one tile = two 32-key units.  K fragments, V^T fragments, S blocks and
+  // P fragments live across the steps below (the next tile's unit-0 K
+  // fragments are read before this tile's last unit is finished).
+  Frag8 kf[NKK];
+  VF vf[2][NDB];
+  f32x16 s0, s1;
+  bf16x8 pb[2];
+  float mt1 = 0.f;
+  // buffer byte offset: compile-time constant UB, or -1 for the runtime buf
+  auto boff_of = [&](auto UB, int buf_rt) __attribute__((always_inline)) {
     constexpr int UBV = decltype(UB)::value;
-    const uint32_t boff = UBV >= 0 ? (uint32_t)(UBV * TILEB) : (uint32_t)(buf_rt * TILEB);
-    const char* smb = sm + boff;
-    bool tree = false;
-    int nvalid = KT;
-    if constexpr (MK) {
-      tree = it >= npre;
+    return UBV >= 0 ? (uint32_t)(UBV * TILEB) : (uint32_t)(buf_rt * TILEB);
+  };
+  auto load_k = [&](uint32_t boff, int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) kf[kk].u = *(const uint4*)(sm + boff + kl[kk] + kb * 32 * ROWB);
+  };
+  auto load_v = [&](uint32_t boff, int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ksub = 0; ksub < 2; ++ksub)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          vf[ksub][db].h[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16*)(sm + boff + vl[rd][db] + (kb * 32 + 16 * ksub) * ROWB));
+  };
+  // S^T block: lane holds keys kb*32 + 8j + 4*hh + i (value s[4j+i]) of query
+  // row lq (one accumulation chain: back-to-back dependent products issue at
+  // full rate)
+  auto qk = [&](f32x16& sr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sr[e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], sr, 0, 0, 0);
+  };
+  // masked keys -> -inf (MK: ragged prefix tile by key index, tree tile by the
+  // ancestor word), then the row maximum in log2 units
+  auto rowmax = [&](auto MASKED, f32x16& sr, int it, int kb) __attribute__((always_inline)) {
+    if constexpr (decltype(MASKED)::value) {
+      const bool tree = it >= npre;
       const int64_t base = tree ? 0 : (int64_t)(t_begin + it) * KT;
-      nvalid = tree ? Tn : (int)min<int64_t>(KT, L - base);
+      const int nvalid = tree ? Tn : (int)min<int64_t>(KT, L - base);
+      const int nv = nvalid - kb * 32;
+      const uint32_t kbits = tree ? (uint32_t)(qmask >> (kb * 32))
+                                  : (nv >= 32 ? 0xffffffffu : (nv <= 0 ? 0u : ((1u << nv) - 1u)));
+      const uint32_t mine = kbits >> (4 * hh);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sr[e] = ((mine >> (8 * (e >> 2) + (e & 3))) & 1u) ? sr[e] : -INFINITY;
     }
-    Frag8 kf[NKK];
-    VF vf[2][NDB];
-    auto load_k = [&](int kb) __attribute__((always_inline)) {
+    float mx = sr[0];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kf[kk].u = *(const uint4*)(smb + kl[kk] + kb * 32 * ROWB);
-    };
-    auto load_v = [&](int kb) __attribute__((always_inline)) {
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sr[e]);
+    return halves_max(mx) * scale_log2;
+  };
+  auto rescale = [&](float mt) __attribute__((always_inline)) {
+    if (mt > mrun + RESCALE_SLACK) {
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mt);
+      lrun *= alpha;
 #pragma unroll
-      for (int ksub = 0; ksub < 2; ++ksub)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int rd = 0; rd < 2; ++rd)
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      mrun = mt;
+    }
+  };
+  // P^T B operand: k-slot t of lane half hh <-> key 16*ksub + 8*(t/4) + 4*hh + t%4,
+  // the same key order as the transposed V^T fragment.  The row sum is a
+  // pairwise tree (independent adds rather than one dependent chain).
+  auto expo = [&](const f32x16& sr) __attribute__((always_inline)) {
+    const float negm = mrun == -INFINITY ? 0.f : -mrun;
+    float p[16];
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            vf[ksub][db].h[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(smb + vl[rd][db] + (kb * 32 + 16 * ksub) * ROWB));
-    };
-    // S^T block: lane holds keys kb*32 + 8j + 4*hh + i (value s[4j+i]) of
-    // query row lq; `split_chain` runs the products as two chains (even and
-    // odd k-steps) when nothing else fills the gaps between them
-    auto qk = [&](f32x16& sr, bool split_chain) __attribute__((always_inline)) {
+    for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(sr[e], scale_log2, negm));
+    float t8[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sr[e] = 0.f;
-      if (split_chain) {
-        f32x16 s1;
+    for (int e = 0; e < 8; ++e) t8[e] = p[2 * e] + p[2 * e + 1];
+    lrun += ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
+    pb[0] = pack8(p);
+    pb[1] = pack8(p + 8);
+  };
+  auto pv = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s1[e] = 0.f;
+    for (int ksub = 0; ksub < 2; ++ksub)
 #pragma unroll
-        for (int kk = 0; kk < NKK; kk += 2) {
-          sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], sr, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk + 1].v, qf[kk + 1], s1, 0, 0, 0);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sr[e] += s1[e];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[kk], sr, 0, 0, 0);
-      }
-    };
-    // masked keys -> -inf, then the row maximum in log2 units
-    auto rowmax = [&](f32x16& sr, int kb) __attribute__((always_inline)) {
-      if constexpr (MK) {
-        const int nv = nvalid - kb * 32;
-        const uint32_t kbits = tree ? (uint32_t)(qmask >> (kb * 32))
-                                    : (nv >= 32 ? 0xffffffffu : (nv <= 0 ? 0u : ((1u << nv) - 1u)));
-        const uint32_t mine = kbits >> (4 * hh);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sr[e] = ((mine >> (8 * (e >> 2) + (e & 3))) & 1u) ? sr[e] : -INFINITY;
-      }
-      float mx = sr[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sr[e]);
-      return halves_max(mx) * scale_log2;
-    };
-    auto rescale = [&](float mt) __attribute__((always_inline)) {
-      if (mt > mrun + RESCALE_SLACK) {
-        const float alpha = __builtin_amdgcn_exp2f(mrun - mt);
-        lrun *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-        mrun = mt;
-      }
-    };
-    // P^T B operand: k-slot t of lane half hh <-> key 16*ksub + 8*(t/4) + 4*hh + t%4,
-    // the same key order as the transposed V^T fragment
-    auto expo = [&](const f32x16& sr, bf16x8* pb) __attribute__((always_inline)) {
-      const float negm = mrun == -INFINITY ? 0.f : -mrun;
-      float p[16];
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(sr[e], scale_log2, negm));
-        ps += p[e];
-      }
-      lrun += ps;
-      pb[0] = pack8(p);
-      pb[1] = pack8(p + 8);
-    };
-    auto pv = [&](const bf16x8* pb) __attribute__((always_inline)) {
-#pragma unroll
-      for (int ksub = 0; ksub < 2; ++ksub)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ksub][db].v, pb[ksub], o[db], 0, 0, 0);
-    };
-
-    f32x16 s0, s1;
-    bf16x8 pb[2];
-    // unit 0 products (nothing to overlap yet), then unit 1's K and unit 0's V
-    load_k(0);
-    qk(s0, true);
-    load_k(1);
-    load_v(0);
-    rescale(rowmax(s0, 0));
-    // unit 1 products || unit 0 exponentials; unit 0 P.V || unit 1 maximum
-    qk(s1, false);
-    expo(s0, pb);
-    pv(pb);
-    const float mt1 = rowmax(s1, 1);
+      for (int db = 0; db < NDB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ksub][db].v, pb[ksub], o[db], 0, 0, 0);
+  };
+  // First part of tile it (its unit-0 K fragments already in kf): unit 0's
+  // products, unit 1's products beside unit 0's exponentials, unit 0's P.V
+  // beside unit 1's row maximum, and unit 1's V^T fragments.
+  auto head = [&](auto MASKED, uint32_t boff, int it) __attribute__((always_inline)) {
+    qk(s0);
+    load_k(boff, 1);
+    load_v(boff, 0);
+    rescale(rowmax(MASKED, s0, it, 0));
+    qk(s1);
+    expo(s0);
+    pv();
+    mt1 = rowmax(MASKED, s1, it, 1);
 #pragma unroll
     for (int i = 0; i < NKK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // vector ALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // vector ALU
     }
 #pragma unroll
     for (int i = 0; i < 2 * NDB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
-    load_v(1);
+    load_v(boff, 1);
+  };
+  // Rest of tile it: unit 1's exponentials and P.V.
+  auto tail = [&]() __attribute__((always_inline)) {
     rescale(mt1);
-    expo(s1, pb);
-    pv(pb);
+    expo(s1);
+    pv();
   };
 
-  // ---- pipeline: tiles 0 .. NBUF-2 in flight before the loop; step it waits
-  // for tile it (this wave's loads, then the barrier for everyone's), refills
-  // the buffer that tile it-1 used (free: every wave has passed the barrier, so
-  // is done with it) with tile it+NBUF-1; then tile it is computed.
-  auto pipeline_step = [&](int it) __attribute__((always_inline)) {
-    // loads issued after tile it's: min(NBUF-2, ntile-1-it) tiles; s_waitcnt
-    // encoding: vmcnt[3:0] and [15:14], expcnt and lgkmcnt left at "no wait"
-    if (ntile - 1 - it >= NBUF - 2) {
+  // ---- pipeline.  All NBUF buffers hold tiles: the one being computed and up
+  // to NBUF-1 in flight.  In the middle of tile it (after its last LDS read)
+  // each wave waits for its loads of tile it+1 and for its own LDS reads, the
+  // barrier makes tile it+1 visible to all and frees tile it's buffer (every
+  // wave has read what it needs of it), which is refilled with tile it+NBUF;
+  // tile it+1's unit-0 K fragments are then read while tile it's last unit is
+  // computed.  s_waitcnt encoding: vmcnt[3:0] and [15:14], expcnt [6:4],
+  // lgkmcnt [11:8] (all-ones fields: no wait).
+  auto mid = [&](int it, uint32_t boff_next) __attribute__((always_inline)) {
+    if (it + 1 >= ntile) return;
+    // loads issued after tile it+1's: min(NBUF-2, ntile-2-it) tiles
+    if (ntile - 2 - it >= NBUF - 2) {
       constexpr int WN = (NBUF - 2) * IPW;
-      __builtin_amdgcn_s_waitcnt((WN & 0xf) | (0x7 << 4) | (0xf << 8) | (((WN >> 4) & 0x3) << 14));
+      __builtin_amdgcn_s_waitcnt((WN & 0xf) | (0x7 << 4) | (0x0 << 8) | (((WN >> 4) & 0x3) << 14));
     } else {
-      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
+      __builtin_amdgcn_s_waitcnt(0x7 << 4);
     }
     __syncthreads();
-    if (it + NBUF - 1 < ntile) issue_tile(it + NBUF - 1, (it + NBUF - 1) % NBUF);
+    if (it + NBUF < ntile) issue_tile(it + NBUF, it % NBUF);
+    if (act) load_k(boff_next, 0);
   };
 
+  // prologue: tiles 0 .. NBUF-2, the query fragments, then tile NBUF-1
 #pragma unroll
   for (int t = 0; t < NBUF - 1; ++t)
     if (t < ntile) issue_tile(t, t);
@@ -400,27 +389,35 @@ __global__ __launch_bounds__(NW * 64) void attn_lds_kernel(
       qf[kk] = f.v;
     }
   }
-  // The query loads go out after the first tiles' loads and complete here,
-  // before the tile loop: the compiler counts only its own loads, and its wait
-  // for these, were it placed inside the loop, would also wait for every tile
-  // load issued after them.  The empty asm reads each fragment, so the loads
-  // cannot sink past this point and that wait lands here (it also covers the
-  // prologue tiles, issued just before).
+  // The query loads complete here, before the tile loop: the compiler counts
+  // only its own loads, and its wait for these, were it placed inside the
+  // loop, would also wait for every tile load issued after them.  The empty
+  // asm reads each fragment, so the loads cannot sink past this point and that
+  // wait lands here; it also covers the tile loads issued before them, so
+  // after the barrier below tile 0 is visible to every wave.
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(qf[kk]));
+  if (NBUF - 1 < ntile) issue_tile(NBUF - 1, NBUF - 1);
+  __syncthreads();
+  if (act && ntile > 0) load_k(0, 0);
 
+  // whole prefix tiles with the buffer a compile-time constant, then the
+  // masked ones (ragged last prefix tile, tree tile) with a runtime buffer
   for (int it0 = 0; it0 < nfast; it0 += NBUF) {
     static_for<NBUF>([&](auto UC) __attribute__((always_inline)) {
       constexpr int u = decltype(UC)::value;
       const int it = it0 + u;
       if (it >= nfast) return;
-      pipeline_step(it);
-      if (act) compute(std::false_type{}, UC, 0, it);
+      if (act) head(std::false_type{}, boff_of(UC, 0), it);
+      mid(it, boff_of(std::integral_constant<int, (u + 1) % NBUF>{}, 0));
+      if (act) tail();
     });
   }
   for (int it = nfast; it < ntile; ++it) {
-    pipeline_step(it);
-    if (act) compute(std::true_type{}, std::integral_constant<int, -1>{}, it % NBUF, it);
+    const std::integral_constant<int, -1> rt{};
+    if (act) head(std::true_type{}, boff_of(rt, it % NBUF), it);
+    mid(it, boff_of(rt, (it + 1) % NBUF));
+    if (act) tail();
   }
 
   // ---- epilogue: O^T lane layout is rows dh = db*32 + 8j + 4*hh + i of query lq
@@ -486,16 +483,16 @@ int launch_attn_stream(int Dh, int nw, dim3 grid, hipStream_t stream, const bf16
                        const uint64_t* anc, int T, int Hq, int Hkv, int n_rchunks, float scale_log2, int n_splits,
                        bf16_t* out, float* ws_o, float* ws_ml) {
   if (Dh != 128 && Dh != 64) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: streaming kernel takes Dh 64 or 128");
-  // Tile depth: three buffers when every workgroup has a compute unit to
-  // itself (deeper prefetch for short per-workgroup runs), else two (half the
-  // LDS).  MEDUSA_ATTN_NBUF = 2 | 3 | 4 forces a depth (tuning runs).
+  // Tile depth: two buffers (one tile computed while the next streams in; a
+  // deeper ring measured no faster and delays the first tile of short
+  // per-workgroup runs).  MEDUSA_ATTN_NBUF = 2 | 3 | 4 forces a depth (tuning
+  // runs).
   static const int forced_nbuf = [] {
     const char* e = getenv("MEDUSA_ATTN_NBUF");
     const int v = e ? atoi(e) : 0;
     return v == 2 || v == 3 || v == 4 ? v : 0;
   }();
-  const long wgs = (long)grid.x * grid.y * grid.z;
-  const int nbuf = forced_nbuf ? forced_nbuf : (wgs <= 256 ? 3 : 2);
+  const int nbuf = forced_nbuf ? forced_nbuf : 2;
 #define LD(NWV)                                                                                                      \
   do {                                                                                                               \
     if (nbuf == 2) launch_d<NWV, 2>(Dh, grid, stream, q, Kc, Vc, Lmax, seq_len, Kt, Vt, anc, T, Hq, Hkv, n_rchunks, \
