@@ -17,6 +17,10 @@ Also measured (same JSON line):
                  matches it.  `step_projections` adds every projection of one step.
   tree_attention the attention kernel alone at batch 8, 32/8 heads, prefix 65536, and
                  at batch 1, prefix 1024, against 8 TB/s
+  heads_all_tree_nodes
+                 medusa_heads_topk on the hidden states of every node of 8 sequences'
+                 64-node trees (512 rows: the heads applied inside the verify forward),
+                 against the 2.5 PFLOP/s dense bf16 peak
   cpu_baseline   the oracle on the host cores on a bounded sample of the same step
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -37,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFS = 2500.0  # dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_gate_up_M64_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "speculative_decoding_heads_amd", "csrc", "gemm.hip")
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
@@ -337,6 +342,26 @@ def main():
     log("tree_attention B8 L65536: %.1f us, %.1f GB/s; B1 L1024: %.1f us, %.1f GB/s" %
         (a64_ms * 1e3, a64_gbs, a1k_ms * 1e3, a1k_gbs))
 
+    # ---- the Medusa heads on every node of 8 sequences' trees (M = 8 * 64 = 512 hidden
+    # states): the heads' products in the compute-bound regime (square-tile kernel)
+    Bh = 8 * T
+    hh = torch_normal((Bh, cfg.d), 1.0, 77, dev, torch.bfloat16)
+    hidx = torch.empty((Bh, cfg.n_medusa, 10), dtype=torch.int32, device=dev)
+    hval = torch.empty((Bh, cfg.n_medusa, 10), dtype=torch.float32, device=dev)
+    hws = torch.empty(max(1, lib().medusa_heads_topk_workspace_size(1, Bh, cfg.d, cfg.vocab, cfg.n_medusa, 10)),
+                      dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        api.medusa_heads_topk(hh, heads["W1"], heads["W2"], 10, topk_idx=hidx, topk_val=hval, ws=hws)
+    torch.cuda.synchronize()
+    hreps = 10
+    with Timer() as th:
+        for _ in range(hreps):
+            api.medusa_heads_topk(hh, heads["W1"], heads["W2"], 10, topk_idx=hidx, topk_val=hval, ws=hws)
+    heads_ms = th.ms() / hreps
+    heads_flop = 2.0 * Bh * cfg.n_medusa * (cfg.d * cfg.d + cfg.vocab * cfg.d)
+    heads_tfs = heads_flop / (heads_ms * 1e-3) / 1e12
+    log("heads on all tree nodes (M %d): %.1f us, %.1f TFLOP/s" % (Bh, heads_ms * 1e3, heads_tfs))
+
     # ---- oracle on the host cores, bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
@@ -376,6 +401,11 @@ def main():
                           "unit": "GB/s", "frac": round(a64_gbs / HBM_PEAK_GBS, 4), "bytes": a64_b},
             "B1_L1024": {"us": round(a1k_ms * 1e3, 2), "achieved": round(a1k_gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(a1k_gbs / HBM_PEAK_GBS, 4), "bytes": a1k_b}},
+        "heads_all_tree_nodes": {
+            "kernels": "gemm_tile_kernel (W1 with the SiLU residual, W2 to fp32 logits) + top-K",
+            "rows": Bh, "bound": "mfma", "us": round(heads_ms * 1e3, 2), "achieved": round(heads_tfs, 1),
+            "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(heads_tfs / MFMA_PEAK_TFS, 4),
+            "flop": heads_flop},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

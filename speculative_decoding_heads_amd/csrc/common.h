@@ -85,4 +85,12 @@ int gemm_qkv_rope_bf16(int B, int T, int K, int Hq, int Hkv, int Dh, const bf16_
                        const int32_t* pos, const float* cos_t, const float* sin_t, int max_pos, bf16_t* q_out,
                        bf16_t* k_out, bf16_t* v_out, hipStream_t stream);
 
+// Square-tile bf16 product for many rows (gemm_tile.hip): M >= GEMM_TILE_MIN_M,
+// K % 32 == 0, every epilogue but SwiGLU; W is [N, K] with K contiguous.
+constexpr int GEMM_TILE_MIN_M = 192;
+bool gemm_tile_takes(int M, int N, int K, int epilogue);
+int gemm_tile_bf16(int M, int N, int K, const bf16_t* A, int64_t lda, int64_t strideA, const bf16_t* W,
+                   int64_t strideW, int epilogue, void* C, int64_t ldc, int64_t strideC, const bf16_t* R, int64_t ldr,
+                   int64_t strideR, int batch, hipStream_t stream);
+
 }  // namespace medusa

@@ -703,6 +703,12 @@ extern "C" int medusa_gemm(int dtype, int M, int N, int K, const void* A, int64_
   MEDUSA_REQUIRE(K % GK == 0, MEDUSA_ERR_UNSUPPORTED, "gemm: bf16 needs K %% 32 == 0 (K=%d)", K);
   MEDUSA_REQUIRE(lda % 8 == 0 && strideA % 8 == 0 && strideW % 8 == 0, MEDUSA_ERR_UNSUPPORTED,
                  "gemm: bf16 rows must be 16-byte aligned");
+  // many rows: the square-tile kernel (compute-bound regime); MEDUSA_GEMM_TILE=0
+  // keeps the streaming kernels for tuning runs
+  static const int e_tile = env_int("MEDUSA_GEMM_TILE", 1);
+  if (e_tile && gemm_tile_takes(M, N, K, epilogue))
+    return gemm_tile_bf16(M, N, K, (const bf16_t*)A, lda, strideA, (const bf16_t*)W, strideW, epilogue, C, ldc,
+                          strideC, (const bf16_t*)R, ldr, strideR, batch, stream);
   GemmPlan p = gemm_plan(M, N, K, batch);
   MEDUSA_REQUIRE(ws_bytes >= p.part_bytes && (p.SK == 1 || ws), MEDUSA_ERR_WORKSPACE, "gemm: workspace %zu < %zu",
                  ws_bytes, p.part_bytes);

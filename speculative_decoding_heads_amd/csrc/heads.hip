@@ -83,15 +83,69 @@ struct LaneList {
   }
 };
 
-// stage 1: grid (n_chunks, M), one wave per chunk of a row -> K candidates per chunk
+// stage 1: grid (n_chunks, M), one wave per chunk of a row -> K candidates per
+// chunk, in two passes over the chunk.  Pass 1 takes each lane's maximum; the
+// K-th largest of the 64 lane maxima, t, is a lower bound of the chunk's K-th
+// largest value (K lanes each hold an entry >= t).  Pass 2 (the chunk is now in
+// L2) inserts only the entries >= t into the lane lists, so the sorted-list
+// insertion, which a wave executes whenever any of its lanes needs it, runs
+// for a few entries per chunk instead of for most of them.  With vec (rows
+// 16-byte aligned, chunk % 256 == 0) lanes read float4 batches, 8 per lane in
+// flight together.
 __global__ __launch_bounds__(64) void topk_stage1_kernel(int V, int chunk, const float* __restrict__ x, int K,
-                                                         float* __restrict__ cv, int* __restrict__ ci) {
+                                                         float* __restrict__ cv, int* __restrict__ ci, int vec) {
   const int ch = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
   const float* r = x + (size_t)row * V;
   const int k0 = ch * chunk, k1 = min(k0 + chunk, V);
+  const int lane = threadIdx.x;
+  constexpr int BATCH = 8 * 4 * 64;  // entries per wave and float4 batch
+  // visit every entry of the chunk: batches of float4, then a scalar tail
+  auto scan = [&](auto&& f) __attribute__((always_inline)) {
+    int k = k0;
+    if (vec) {
+      for (; k + BATCH <= k1; k += BATCH) {
+        float4 b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) b[u] = *(const float4*)(r + k + 256 * u + 4 * lane);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int kb = k + 256 * u + 4 * lane;
+          f(b[u].x, kb);
+          f(b[u].y, kb + 1);
+          f(b[u].z, kb + 2);
+          f(b[u].w, kb + 3);
+        }
+      }
+    }
+    for (k += lane; k < k1; k += 64) f(r[k], k);
+  };
+  float lm = -INFINITY;
+  scan([&](float v, int) __attribute__((always_inline)) { lm = fmaxf(lm, v); });
+  // K-th largest lane maximum (each round removes the largest, lowest lane first)
+  float t = -INFINITY;
+  {
+    float v = lm;
+    for (int rd = 0; rd < K; ++rd) {
+      float bv = v;
+      int bl = lane;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(bv, o, 64);
+        const int l2 = __shfl_xor(bl, o, 64);
+        if (v2 > bv || (v2 == bv && l2 < bl)) {
+          bv = v2;
+          bl = l2;
+        }
+      }
+      t = bv;
+      if (lane == bl) v = -INFINITY;
+    }
+  }
   LaneList L;
   L.init();
-  for (int k = k0 + (int)threadIdx.x; k < k1; k += 64) L.insert(r[k], k);
+  scan([&](float v, int k) __attribute__((always_inline)) {
+    if (v >= t) L.insert(v, k);
+  });
   const size_t o = ((size_t)row * nch + ch) * K;
   L.pop_k(K, cv + o, ci + o);
 }
@@ -115,13 +169,19 @@ __global__ __launch_bounds__(64) void topk_stage2_kernel(int ncand, const float*
   }
 }
 
-int topk_chunks(int V) {
-  int n = (V + 64 * TK_PER_LANE - 1) / (64 * TK_PER_LANE);
+// Chunks per row: 512-entry chunks (TK_PER_LANE entries per lane) while the
+// rows are few; with many rows fewer, longer chunks (about 4096 waves in all),
+// so that each wave's fixed cost of handing on K candidates is spread over more
+// entries.
+int topk_chunks(int M, int V) {
+  const int nmax = (V + 64 * TK_PER_LANE - 1) / (64 * TK_PER_LANE);
+  int n = (4096 + M - 1) / M;
+  if (n > nmax) n = nmax;
   return n < 1 ? 1 : (n > 1024 ? 1024 : n);
 }
 
 size_t topk_ws(int M, int V, int K) {
-  return align_up((size_t)M * topk_chunks(V) * K * (sizeof(float) + sizeof(int)), 256);
+  return align_up((size_t)M * topk_chunks(M, V) * K * (sizeof(float) + sizeof(int)), 256);
 }
 
 struct HeadsLayout {
@@ -156,11 +216,13 @@ extern "C" int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* id
   MEDUSA_REQUIRE(x && idx, MEDUSA_ERR_ARG, "topk_rows: null pointer");
   MEDUSA_REQUIRE(ws && ws_bytes >= topk_ws(M, V, K), MEDUSA_ERR_WORKSPACE, "topk_rows: workspace %zu < %zu", ws_bytes,
                  topk_ws(M, V, K));
-  const int nch = topk_chunks(V);
-  const int chunk = (V + nch - 1) / nch;
+  const int nch = topk_chunks(M, V);
+  int chunk = (V + nch - 1) / nch;
+  const int vec = V % 4 == 0 && ((uintptr_t)x & 15) == 0;
+  if (vec) chunk = (chunk + 255) / 256 * 256;  // batches start 16-byte aligned
   float* cv = (float*)ws;
   int* ci = (int*)((char*)ws + (size_t)M * nch * K * sizeof(float));
-  hipLaunchKernelGGL(topk_stage1_kernel, dim3(nch, M), dim3(64), 0, stream, V, chunk, x, K, cv, ci);
+  hipLaunchKernelGGL(topk_stage1_kernel, dim3(nch, M), dim3(64), 0, stream, V, chunk, x, K, cv, ci, vec);
   int rc = check_launch("topk_rows stage 1");
   if (rc) return rc;
   hipLaunchKernelGGL(topk_stage2_kernel, dim3(M), dim3(64), 0, stream, nch * K, cv, ci, K, idx, val);

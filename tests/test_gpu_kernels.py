@@ -151,11 +151,32 @@ def test_kv_compact_bit_exact(dev, dtype_name):
     assert to_np(n_out).tolist() == [5, 7, 16, 4]
 
 
+def _check_heads_topk(gi, gv, ref_logits):
+    """Logits at the returned indices match the oracle; indices bit-exact except
+    where the oracle's own ranking has a near-tie at the measured error level."""
+    ref_idx = topk_desc(ref_logits, 10)
+    B, H = ref_logits.shape[:2]
+    err = 0.0
+    for b in range(B):
+        for k in range(H):
+            rl = ref_logits[b, k]
+            assert_close(gv[b, k], rl[gi[b, k]], rtol=2e-2, atol=1e-2, what="topk values")
+            err = max(err, float(np.abs(gv[b, k] - rl[gi[b, k]]).max()))
+    mism = 0
+    for b in range(B):
+        for k in range(H):
+            if gi[b, k].tolist() != ref_idx[b, k].tolist():
+                # allowed only where the reference ranking has a gap below the measured error
+                kth = np.sort(ref_logits[b, k])[::-1]
+                gap = np.min(np.abs(np.diff(kth[:11])))
+                assert gap <= 4 * err + 1e-7, "top-K mismatch without near-tie (b=%d k=%d)" % (b, k)
+                mism += 1
+    assert mism <= max(B, 1)
+
+
 @pytest.mark.parametrize("B", [1, 8])
 def test_heads_topk_bf16_full_size(dev, B):
-    """Medusa heads at d 4096, V 32000, 4 heads, top-10 (bf16): logits at the returned
-    indices match the oracle; indices bit-exact except where the oracle's own ranking
-    has a near-tie at the error level."""
+    """Medusa heads at d 4096, V 32000, 4 heads, top-10 (bf16) against the oracle."""
     import torch
     from speculative_decoding_heads_amd import api
     say("medusa_heads_topk bf16 B", B)
@@ -165,24 +186,23 @@ def test_heads_topk_bf16_full_size(dev, B):
     torch.cuda.synchronize()
     # the ranking is decided on float32 logits on both sides
     ref_logits = medusa_heads_logits(h, W1, W2, bf16=True).astype(np.float32).astype(np.float64)
-    gi, gv = to_np(idx), to_np(val)
-    ref_idx = topk_desc(ref_logits, 10)
-    err = 0.0
-    for b in range(B):
-        for k in range(4):
-            rl = ref_logits[b, k]
-            assert_close(gv[b, k], rl[gi[b, k]], rtol=2e-2, atol=1e-2, what="topk values")
-            err = max(err, float(np.abs(gv[b, k] - rl[gi[b, k]]).max()))
-    mism = 0
-    for b in range(B):
-        for k in range(4):
-            if gi[b, k].tolist() != ref_idx[b, k].tolist():
-                # allowed only where the reference ranking has a gap below the measured error
-                kth = np.sort(ref_logits[b, k])[::-1]
-                gap = np.min(np.abs(np.diff(kth[:11])))
-                assert gap <= 4 * err + 1e-7, "top-K mismatch without near-tie (b=%d k=%d)" % (b, k)
-                mism += 1
-    assert mism <= B
+    _check_heads_topk(to_np(idx), to_np(val), ref_logits)
+
+
+def test_heads_topk_bf16_all_tree_nodes(dev):
+    """The heads on every node of 8 sequences' 64-node trees (512 hidden states, the
+    square-tile product path), full d / V / H; the oracle checks 6 sampled rows."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    B = 512
+    say("medusa_heads_topk bf16 B", B)
+    h, W1, W2 = heads_weights(seed=3, B=B)
+    tdt = torch.bfloat16
+    idx, val = api.medusa_heads_topk(to_dev(h, tdt, dev), to_dev(W1, tdt, dev), to_dev(W2, tdt, dev), 10)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 400, 511]
+    ref_logits = medusa_heads_logits(h[rows], W1, W2, bf16=True).astype(np.float32).astype(np.float64)
+    _check_heads_topk(to_np(idx)[rows], to_np(val)[rows], ref_logits)
 
 
 def test_heads_topk_fp32_small(dev):
@@ -201,7 +221,11 @@ def test_heads_topk_fp32_small(dev):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (8, 1000, 512), (64, 12288, 4096), (64, 4096, 11008),
-                                   (100, 384, 256), (512, 512, 4096), (40, 1000, 1056), (33, 200, 96)])
+                                   (100, 384, 256), (512, 512, 4096), (40, 1000, 1056), (33, 200, 96),
+                                   # square-tile path (M >= 192): ragged M and N tiles, one chunk, a chunk
+                                   # count that is not a multiple of the LDS ring
+                                   (300, 1000, 512), (192, 256, 32), (700, 300, 96), (512, 4096, 4096),
+                                   (768, 16484, 256)])
 def test_gemm_bf16(dev, M, N, K):
     import torch
     from speculative_decoding_heads_amd import api
@@ -217,18 +241,18 @@ def test_gemm_bf16(dev, M, N, K):
     assert_close(to_np(out), ref, rtol=1e-4, atol=1e-4, what="gemm")
 
 
-@pytest.mark.parametrize("dtype_name", ["bf16", "fp32"])
-def test_gemm_epilogues(dev, dtype_name):
+@pytest.mark.parametrize("dtype_name,M", [("bf16", 5), ("fp32", 5), ("bf16", 260)])
+def test_gemm_epilogues(dev, dtype_name, M):
     import torch
     from speculative_decoding_heads_amd import api
     from speculative_decoding_heads_amd._lib import EPI_RESID, EPI_SILU_RESID_A, EPI_STORE, EPI_SWIGLU
     from workloads import bf16_round
-    say("gemm epilogues", dtype_name)
+    say("gemm epilogues", dtype_name, "M", M)
     tdt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
     rnd = bf16_round if dtype_name == "bf16" else (lambda x: x)
     tol = dict(rtol=2e-2, atol=1e-2) if dtype_name == "bf16" else dict(rtol=1e-5, atol=1e-5)
     rng = np.random.default_rng(1)
-    M, K = 5, 256
+    K = 256
     A = rnd(rng.standard_normal((M, K)).astype(np.float32))
     W = rnd((rng.standard_normal((512, K)) * 0.05).astype(np.float32))
     R = rnd(rng.standard_normal((M, 512)).astype(np.float32))
@@ -289,3 +313,20 @@ def test_argmax_and_topk_rows_ties(dev):
     torch.cuda.synchronize()
     assert to_np(am).tolist() == [5, int(x[1].argmax()), 999]
     assert np.array_equal(to_np(idx), topk_desc(x, 5))
+
+
+@pytest.mark.parametrize("M,V", [(100, 5000), (2048, 9000), (7, 1001)])
+def test_topk_rows_many_rows(dev, M, V):
+    """Many rows take longer chunks per wave in the first stage (batched float4 reads
+    plus a scalar tail; V % 4 != 0 reads scalars only); ties still go to the lower
+    index (values drawn from a small set so that ties are common)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("topk rows M", M, "V", V)
+    rng = np.random.default_rng(M)
+    x = rng.integers(-50, 50, size=(M, V)).astype(np.float32) / 8.0
+    idx, val = api.topk_rows(torch.from_numpy(x).to(dev), 10)
+    torch.cuda.synchronize()
+    want = topk_desc(x, 10)
+    assert np.array_equal(to_np(idx), want)
+    assert np.array_equal(to_np(val), np.take_along_axis(x, want, -1))
