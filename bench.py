@@ -388,7 +388,7 @@ def main():
         "accepted_tok_per_s": round(steps_per_s * mean_tokens, 2),
         "wall_ms_per_step": round(wall_ms, 4),
         "launch": launch,
-        "roofline": {"kernel": "gemm_lds_kernel<2,2,4>: gate/up projection, M 64, N 22016, K 4096, SwiGLU",
+        "roofline": {"kernel": "gemm_lds_kernel<2,2,4,3>: gate/up projection, M 64, N 22016, K 4096, SwiGLU",
                      "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},

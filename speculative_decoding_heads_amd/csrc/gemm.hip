@@ -361,7 +361,8 @@ __global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, co
   store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
 }
 
-// Kernel for M > 32.  The four waves of a workgroup own neighbouring
+// Kernel for M > 32.  The NWV waves of a workgroup (4, or 3 when 96-row
+// workgroup tiles spread a product more evenly over the CUs) own neighbouring
 // (NR*16)-row W tiles and walk the same k range; the workgroup stages the 64 A
 // rows of each chunk (U k-steps) once in LDS, so A costs one global read per
 // workgroup instead of one per wave (re-reading A per wave caps these products
@@ -374,15 +375,18 @@ __global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, co
 //     workgroup per CU there is no other wave to cover it).
 // Staged rows are padded by 16 bytes so the 16 rows that one ds_read_b128
 // touches fall in distinct banks.  A K split across workgroups (SK > 1) leaves
-// fp32 partials.  grid (N tiles of 4*NR*16 rows, m tiles * SK, batch).
-template <int NR, int U, int NS>
-__global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, const bf16_t* __restrict__ A, int64_t lda,
-                                                        int64_t sA, const bf16_t* __restrict__ W, int64_t sW, int SK,
-                                                        EpiArgs e, int64_t sC, int64_t sR, float* __restrict__ part) {
+// fp32 partials.  grid (N tiles of NWV*NR*16 rows, m tiles * SK, batch).
+template <int NR, int U, int NS, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gemm_lds_kernel(int M, int N, int K, const bf16_t* __restrict__ A,
+                                                            int64_t lda, int64_t sA, const bf16_t* __restrict__ W,
+                                                            int64_t sW, int SK, EpiArgs e, int64_t sC, int64_t sR,
+                                                            float* __restrict__ part) {
   constexpr int MB = 4, TN = NR * 16;
+  constexpr int NTHR = NWV * 64;
   constexpr int ROWB = U * GK * 2 + 16;  // bytes per staged A row
   constexpr int PPR = U * GK * 2 / 16;   // 16-byte pieces per A row and chunk
-  constexpr int PPT = GM * PPR / GTHR;   // pieces per thread and chunk (= U)
+  constexpr int NPC = GM * PPR;          // pieces per chunk
+  constexpr int PPT = (NPC + NTHR - 1) / NTHR;  // pieces per thread and chunk (the last ones partly idle)
   constexpr int BUFB = GM * ROWB;
   static_assert(NS >= 4 && NS % 2 == 0, "the staging distance needs NS >= 4, even");
   // three A buffers; the rotary epilogue reuses them for a 4 x 16 x 64 fp32 exchange
@@ -398,8 +402,8 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
   // EPI_QKV_ROPE maps the four 16-row wave tiles to two blocks of the first
   // half of one head's rows and the same blocks of the second half (waves
   // w and w ^ 1 hold the two rotary partners of the same dimensions)
-  const bool rope = e.mode == EPI_QKV_ROPE;
-  int n0 = (nt * 4 + w) * TN;
+  const bool rope = NWV == 4 && e.mode == EPI_QKV_ROPE;
+  int n0 = (nt * NWV + w) * TN;
   if (rope) {
     const int wg_per_head = e.Dh / 64, hd = nt / wg_per_head, sub = nt % wg_per_head;
     n0 = hd * e.Dh + (w & 1) * (e.Dh / 2) + (sub * 2 + (w >> 1)) * 16;
@@ -423,12 +427,13 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
   const bf16_t* wrow[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) wrow[i] = W + (size_t)min(n0 + i * 16 + l16, N - 1) * K + lg * 8;
-  // GM * PPR pieces per chunk: thread tid stages pieces tid + GTHR*q
+  // NPC pieces per chunk: thread tid stages pieces tid + NTHR*q (< NPC; a
+  // thread past the last piece loads a valid one and does not store it)
   const bf16_t* apiece[PPT];
   int aoff[PPT];
 #pragma unroll
   for (int q = 0; q < PPT; ++q) {
-    const int pc = tid + GTHR * q, r = pc / PPR, cp = pc % PPR;
+    const int pc = min(tid + NTHR * q, NPC - 1), r = pc / PPR, cp = pc % PPR;
     apiece[q] = A + (size_t)min(m0 + r, M - 1) * lda + cp * 8;
     aoff[q] = r * ROWB + cp * 16;
   }
@@ -460,7 +465,8 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
   };
   auto stage = [&](int buf, const Stage& st) {
 #pragma unroll
-    for (int q = 0; q < PPT; ++q) *(u32x4*)(lds + buf * BUFB + aoff[q]) = st.a[q];
+    for (int q = 0; q < PPT; ++q)
+      if (NPC % NTHR == 0 || tid + NTHR * q < NPC) *(u32x4*)(lds + buf * BUFB + aoff[q]) = st.a[q];
   };
   auto readb = [&](F8 (&b)[U][MB], int buf) {
     const char* base = lds + buf * BUFB + boff;
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(GTHR) void gemm_lds_kernel(int M, int N, int K, con
     for (; v + NS + 1 < per; v += NS) seq(full_round, v, std::make_integer_sequence<int, NS>{});
     for (; v < per; v += NS) seq(last_round, v, std::make_integer_sequence<int, NS>{});
   }
-  if constexpr (NR == 1) {
+  if constexpr (NR == 1 && NWV == 4) {
     if (rope) {
       rope_epilogue(acc, lds, w, n0, m0, M, e, l16, lg);
       return;
@@ -561,6 +567,7 @@ __global__ void splitk_reduce_kernel(int M, int N, int SK, const float* __restri
 
 struct GemmPlan {
   int SK, MB, NR, U, m_tiles, n_tiles;
+  int NWV;   // gemm_lds_kernel: waves per workgroup (4, or 3 for 96-row tiles)
   bool KW;   // register kernel: the four waves split K
   bool LDS;  // M > 32: A staged in LDS (gemm_lds_kernel)
   size_t part_bytes;
@@ -598,17 +605,38 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
     // workgroups, else 64-row tiles, and split K across workgroups only when
     // even those leave most CUs idle.
     const int64_t per_tile = (int64_t)p.m_tiles * batch;
-    const int64_t wg2 = (N + 127) / 128 * per_tile, wg1 = (N + 63) / 64 * per_tile;
+    const int64_t wg2 = (N + 127) / 128 * per_tile;
+    p.NWV = 4;
     p.NR = e_lnr == 1 || e_lnr == 2 ? e_lnr : (wg2 >= 160 ? 2 : 1);
-    const int wg_rows = 4 * p.NR * 16;
+    if (!e_lnr && !e_sk) {
+      // Workgroup tiles of 128, 96 or 64 rows: the kernel time follows the
+      // rows per CU, so take the one with the fewest rows on the busiest CU
+      // (ceil(workgroups / 256) * rows), the larger tile on a tie, among
+      // shapes that give >= 160 workgroups (fewer take the K split below).
+      // (waves, NR); 96-row tiles as 3 waves x 32 rows (measured faster than 6 x 16)
+      const int cand[3][2] = {{4, 2}, {3, 2}, {4, 1}};
+      int64_t best = -1;
+      for (const auto& c : cand) {
+        const int rows = c[0] * c[1] * 16;
+        const int64_t wgs = (N + rows - 1) / rows * per_tile;
+        if (wgs < 160) continue;
+        const int64_t cost = (wgs + 255) / 256 * rows;
+        if (best < 0 || cost < best) {
+          best = cost;
+          p.NWV = c[0];
+          p.NR = c[1];
+        }
+      }
+    }
+    const int wg_rows = p.NWV * p.NR * 16;
     p.n_tiles = (N + wg_rows - 1) / wg_rows;
     const int64_t wgs = (int64_t)p.n_tiles * per_tile;
     int sk = e_sk > 0 ? e_sk : (wgs >= 160 ? 1 : (int)(256 / wgs));
-    (void)wg1;
     const int nchunks = nsteps / p.U;
     const int skmax = nchunks / 4 > 0 ? nchunks / 4 : 1;
     p.SK = sk < 1 ? 1 : (sk > skmax ? skmax : sk);
   } else {
+    p.NWV = 4;
     p.NR = p.MB == 4 && !e_nr4 ? 2 : 4;
     const int wg_rows = (p.KW ? 1 : 4) * p.NR * 16;
     p.n_tiles = (N + wg_rows - 1) / wg_rows;
@@ -638,16 +666,19 @@ void gemm_bf16_launch(const GemmPlan& p, int M, int N, int K, const void* A, int
     if (p.KW) GEMM_LAUNCH_KW(MBV, NRV, UV, true); \
     else GEMM_LAUNCH_KW(MBV, NRV, UV, false);     \
   } while (0)
-#define GEMM_LAUNCH_LDS(NRV, UV, NSV)                                                                      \
-  hipLaunchKernelGGL((gemm_lds_kernel<NRV, UV, NSV>), grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, lda, \
-                     strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
+#define GEMM_LAUNCH_LDS(NRV, UV, NSV, NWVV)                                                                 \
+  hipLaunchKernelGGL((gemm_lds_kernel<NRV, UV, NSV, NWVV>), grid, dim3(NWVV * 64), 0, stream, M, N, K,          \
+                     (const bf16_t*)A, lda, strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
   if (p.LDS) {
-    if (p.NR == 1) {
-      if (p.U == 2) GEMM_LAUNCH_LDS(1, 2, 4);
-      else GEMM_LAUNCH_LDS(1, 1, 4);
+    if (p.NWV == 3) {
+      if (p.U == 2) GEMM_LAUNCH_LDS(2, 2, 4, 3);
+      else GEMM_LAUNCH_LDS(2, 1, 4, 3);
+    } else if (p.NR == 1) {
+      if (p.U == 2) GEMM_LAUNCH_LDS(1, 2, 4, 4);
+      else GEMM_LAUNCH_LDS(1, 1, 4, 4);
     } else {
-      if (p.U == 2) GEMM_LAUNCH_LDS(2, 2, 4);
-      else GEMM_LAUNCH_LDS(2, 1, 4);
+      if (p.U == 2) GEMM_LAUNCH_LDS(2, 2, 4, 4);
+      else GEMM_LAUNCH_LDS(2, 1, 4, 4);
     }
   } else if (p.MB == 1) {
     if (p.U == 4) GEMM_LAUNCH(1, 4, 4);
@@ -845,6 +876,7 @@ int gemm_qkv_rope_bf16(int B, int T, int K, int Hq, int Hkv, int Dh, const bf16_
   GemmPlan p = gemm_plan(M, N, K, 1);
   if (!p.LDS) return MEDUSA_ERR_UNSUPPORTED;
   p.NR = 1;
+  p.NWV = 4;
   p.SK = 1;
   p.n_tiles = N / 64;
   EpiArgs e{EPI_QKV_ROPE, nullptr, 0, nullptr, 0, A, K, K, 0, pos, cos_t, sin_t, max_pos, T, Hq, Hkv, Dh,

@@ -225,7 +225,9 @@ def test_heads_topk_fp32_small(dev):
                                    # square-tile path (M >= 192): ragged M and N tiles, one chunk, a chunk
                                    # count that is not a multiple of the LDS ring
                                    (300, 1000, 512), (192, 256, 32), (700, 300, 96), (512, 4096, 4096),
-                                   (768, 16484, 256)])
+                                   (768, 16484, 256),
+                                   # streaming path with three-wave 96-row workgroup tiles (ragged last tile)
+                                   (64, 20000, 256)])
 def test_gemm_bf16(dev, M, N, K):
     import torch
     from speculative_decoding_heads_amd import api
@@ -270,6 +272,23 @@ def test_gemm_epilogues(dev, dtype_name, M):
     z = A.astype(np.float64) @ Wsq.astype(np.float64).T
     assert_close(to_np(out), np.concatenate([A, A], 1) + silu(z), what="silu_resid", **tol)
     torch.cuda.synchronize()
+
+
+def test_gemm_swiglu_96_row_tiles(dev):
+    """The gate/up shape of the 7B verify forward (N 22016) takes three-wave 96-row
+    workgroup tiles; SwiGLU pairs rows 2j (gate) and 2j+1 (up)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import EPI_SWIGLU
+    from workloads import bf16_round
+    say("gemm swiglu 64 x 22016 x 256")
+    rng = np.random.default_rng(7)
+    A = bf16_round(rng.standard_normal((64, 256)).astype(np.float32))
+    W = bf16_round((rng.standard_normal((22016, 256)) * 0.05).astype(np.float32))
+    out = api.gemm(to_dev(A, torch.bfloat16, dev), to_dev(W, torch.bfloat16, dev), EPI_SWIGLU)
+    torch.cuda.synchronize()
+    acc = A.astype(np.float64) @ W.astype(np.float64).T
+    assert_close(to_np(out), silu(acc[:, 0::2]) * acc[:, 1::2], what="swiglu", rtol=2e-2, atol=1e-2)
 
 
 @pytest.mark.parametrize("dtype_name,M,N,K", [("bf16", 64, 4096, 4096), ("bf16", 64, 4096, 11008),
