@@ -17,6 +17,8 @@ Also measured (same JSON line):
                  matches it.  `step_projections` adds every projection of one step.
   tree_attention the attention kernel alone at batch 8, 32/8 heads, prefix 65536, and
                  at batch 1, prefix 1024, against 8 TB/s
+  prefix_sweep   the same step (eager launches) at prefixes 4k, 16k and 64k, the cache
+                 filled with N(0,1) keys and values (5 timed steps each)
   heads_all_tree_nodes
                  medusa_heads_topk on the hidden states of every node of 8 sequences'
                  64-node trees (512 rows: the heads applied inside the verify forward),
@@ -62,6 +64,8 @@ def parse():
     p.add_argument("--attn-reps", type=int, default=20)
     p.add_argument("--roofline-only", action="store_true")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--sweep", type=str, default="4096,16384,65536",
+                   help="longer prefixes at which the same step is also timed ('' for none)")
     return p.parse_args()
 
 
@@ -170,7 +174,8 @@ def main():
     log("generating %d-layer 7B-shaped weights on device" % NL)
     params, heads = model_weights_torch(cfg, 1, dev, torch.bfloat16, n_layers=NL)
     sample_layers = [{k: v for k, v in params["layers"][i].items()} for i in range(min(4, NL))]
-    model = Model(params, heads, max_pos=args.prefix + 512)
+    sweep_L = [int(x) for x in args.sweep.split(",") if x.strip()]
+    model = Model(params, heads, max_pos=max([args.prefix] + sweep_L) + 512)
     for l in params["layers"]:
         for k in ("wq", "wk", "wv", "w_gate", "w_up"):
             l[k] = None
@@ -255,6 +260,41 @@ def main():
     steps_per_s = 1e3 / step_ms
     log("step %.3f ms (wall %.3f ms), %.1f steps/s, mean tokens/step %.2f" % (step_ms, wall_ms, steps_per_s,
                                                                               mean_tokens))
+
+    # ---- the same step at longer prefixes: the cache holds N(0,1) keys and values
+    # (its contents do not change the work), the prefix length is set directly
+    sweep = {}
+    for Ls in sweep_L:
+        st2 = State(model, B, Ls + 128, 64)
+        for l in range(NL):
+            st2.Kc[l].normal_()
+            st2.Vc[l].normal_()
+        st2.h_sel.copy_(st.h_sel)
+        st2.root.copy_(st.root)
+        seq2 = torch.full((B,), Ls, dtype=torch.int32, device=dev)
+        ws2 = torch.empty(step_workspace_size(model, tree, B, Ls + 128), dtype=torch.uint8, device=dev)
+
+        def sweep_step():
+            st2.seq_len.copy_(seq2)
+            st2.n_out.zero_()
+            step(model, tree, st2, TYPICAL, tau, eps, delta, L_hint=Ls + 128, ws=ws2)
+
+        for _ in range(2):
+            sweep_step()
+        torch.cuda.synchronize()
+        acc_sum.zero_()
+        nrep = 5
+        with Timer() as tw:
+            for _ in range(nrep):
+                sweep_step()
+                acc_sum += st2.accept_len
+        ms = tw.ms() / nrep
+        toks = float(acc_sum.sum()) / (nrep * B) + 1.0
+        sweep[str(Ls)] = {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 3),
+                          "accepted_tokens_per_step": round(toks, 3), "accepted_tok_per_s": round(1e3 / ms * toks, 2)}
+        log("prefix %d: %.3f ms/step, %.1f steps/s" % (Ls, ms, 1e3 / ms))
+        del st2, ws2
+        torch.cuda.empty_cache()
 
     # ---- dominant kernel: the gate/up projection at M = 64 rows, over the 32 layers' weights
     T = tree.T
@@ -401,6 +441,7 @@ def main():
                           "unit": "GB/s", "frac": round(a64_gbs / HBM_PEAK_GBS, 4), "bytes": a64_b},
             "B1_L1024": {"us": round(a1k_ms * 1e3, 2), "achieved": round(a1k_gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(a1k_gbs / HBM_PEAK_GBS, 4), "bytes": a1k_b}},
+        "prefix_sweep": sweep,
         "heads_all_tree_nodes": {
             "kernels": "gemm_tile_kernel (W1 with the SiLU residual, W2 to fp32 logits) + top-K",
             "rows": Bh, "bound": "mfma", "us": round(heads_ms * 1e3, 2), "achieved": round(heads_tfs, 1),
