@@ -295,6 +295,20 @@ __global__ __launch_bounds__(TTHR) void gemm_tile_kernel(int M, int N, int K, co
   }
 }
 
+
+// compute units of the current device (cached per device)
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 bool gemm_tile_takes(int M, int N, int K, int epilogue) {
@@ -310,15 +324,21 @@ int gemm_tile_bf16(int M, int N, int K, const bf16_t* A, int64_t lda, int64_t st
   MEDUSA_REQUIRE((int64_t)256 * lda * 2 < (1ll << 31) && (int64_t)TBN * K * 2 < (1ll << 31), MEDUSA_ERR_UNSUPPORTED,
                  "gemm tile: rows too long");
   TileEpi e{epilogue, C, ldc, strideC, R, ldr, strideR, A, lda, strideA, K};
-  // 256-row tiles unless they leave three quarters of the 256 CUs idle (the
-  // 128-row tiles read twice the LDS bytes per product: slower per workgroup)
   const int64_t tiles256 = (int64_t)((M + 255) / 256) * ((N + TBN - 1) / TBN) * batch;
   const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + TBN - 1) / TBN) * batch;
   MEDUSA_REQUIRE(tiles128 < (1ll << 31), MEDUSA_ERR_UNSUPPORTED, "gemm tile: too many tiles");
+  // One workgroup per CU at a time (its LDS takes most of the CU's 160 KB),
+  // so the time goes as the number of rounds of workgroups times the time of
+  // one tile; a 128-row tile takes about 0.7 of a 256-row one (half the
+  // products, but each W byte staged for half as many rows).
+  const int64_t ncu = cu_count();
+  const int64_t rounds256 = (tiles256 + ncu - 1) / ncu, rounds128 = (tiles128 + ncu - 1) / ncu;
+  const bool bm256 = rounds128 * 7 >= rounds256 * 10;
   // k chunk of 64 (whole 128-byte lines of each row, two buffers) or of 32
   // (half lines, four buffers)
   static const bool kc32 = getenv("MEDUSA_TILE_KC") && atoi(getenv("MEDUSA_TILE_KC")) == 32;
-  if (tiles256 >= 64) {
+  static const int bm_env = getenv("MEDUSA_TILE_BM") ? atoi(getenv("MEDUSA_TILE_BM")) : 0;
+  if (bm_env == 256 || (bm_env != 128 && bm256)) {
     if (kc32)
       hipLaunchKernelGGL((gemm_tile_kernel<256, 32, 4>), dim3((unsigned)tiles256), dim3(TTHR), 0, stream, M, N, K, A,
                          lda, strideA, W, strideW, e);

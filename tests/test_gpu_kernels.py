@@ -222,10 +222,11 @@ def test_heads_topk_fp32_small(dev):
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (8, 1000, 512), (64, 12288, 4096), (64, 4096, 11008),
                                    (100, 384, 256), (512, 512, 4096), (40, 1000, 1056), (33, 200, 96),
-                                   # square-tile path (M >= 192): ragged M and N tiles, one chunk, a chunk
-                                   # count that is not a multiple of the LDS ring
-                                   (300, 1000, 512), (192, 256, 32), (700, 300, 96), (512, 4096, 4096),
-                                   (768, 16484, 256),
+                                   # square-tile path (M >= 192, K % 64 == 0): 128-row tiles with ragged M
+                                   # and N, a single 64-k chunk, as many chunks as LDS buffers, 256-row
+                                   # tiles with ragged M and N; K % 64 != 0 goes to the streaming path
+                                   (300, 1000, 512), (256, 512, 64), (512, 4096, 4096), (768, 16484, 256),
+                                   (1000, 20000, 128), (192, 256, 32), (700, 300, 96),
                                    # streaming path with three-wave 96-row workgroup tiles (ragged last tile)
                                    (64, 20000, 256)])
 def test_gemm_bf16(dev, M, N, K):
