@@ -9,7 +9,7 @@ reset to 1024 tokens before every step (a device-side copy), so every timed step
 the same workload.
 
 Also measured (same JSON line):
-  roofline       the dominant kernel: gemm_lds_kernel on the gate/up projection of the
+  roofline       the dominant kernel: gemm_dma_kernel on the gate/up projection of the
                  64 tree rows (M 64, N 22016, K 4096, SwiGLU epilogue), the largest
                  single share of the step; average launch time with HIP events over the
                  32 layers' weights, against 8 TB/s; `traffic` from the committed
@@ -44,7 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFS = 2500.0  # dense bf16
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_gate_up_M64_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_dma_gate_up_M64_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "speculative_decoding_heads_amd", "csrc", "gemm.hip")
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 
@@ -130,7 +130,7 @@ def traffic_from(fetch_dir, write_dir):
         for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(fn) as f:
                 rows += [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
-        gemm = [float(r["Counter_Value"]) for r in rows if "gemm_lds_kernel" in r["Kernel_Name"]]
+        gemm = [float(r["Counter_Value"]) for r in rows if "gemm_dma_kernel" in r["Kernel_Name"]]
         copy = [float(r["Counter_Value"]) for r in rows if "gather_rows_kernel" in r["Kernel_Name"]]
         if not gemm or not copy:
             raise SystemExit("no %s samples for the GEMM or the copy in %s" % (counter, d))
@@ -141,7 +141,7 @@ def traffic_from(fetch_dir, write_dir):
     ref_kib = COPY_BYTES / 1024.0
     sf, sw = ref_kib / c_f, ref_kib / c_w
     fetch_b, write_b = g_f * sf * 1024.0, g_w * sw * 1024.0
-    out = {"kernel": "gemm_lds_kernel gate/up M64 N22016 K4096", "source_sha256": source_sha(),
+    out = {"kernel": "gemm_dma_kernel gate/up M64 N22016 K4096", "source_sha256": source_sha(),
            "fetch_kib_raw": g_f, "write_kib_raw": g_w, "copy_fetch_kib_raw": c_f, "copy_write_kib_raw": c_w,
            "copy_bytes": COPY_BYTES, "fetch_scale": sf, "write_scale": sw,
            "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
@@ -428,11 +428,11 @@ def main():
         "accepted_tok_per_s": round(steps_per_s * mean_tokens, 2),
         "wall_ms_per_step": round(wall_ms, 4),
         "launch": launch,
-        "roofline": {"kernel": "gemm_lds_kernel<2,2,4,3>: gate/up projection, M 64, N 22016, K 4096, SwiGLU",
+        "roofline": {"kernel": "gemm_dma_kernel<2,3,7>: gate/up projection, M 64, N 22016, K 4096, SwiGLU",
                      "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},
-        "step_projections": {"kernels": "gemm_lds_kernel + resid_rmsnorm_kernel: every projection of one step",
+        "step_projections": {"kernels": "gemm_dma_kernel + resid_rmsnorm_kernel: every projection of one step",
                              "achieved": round(gemm_gbs, 1), "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
                              "bytes_per_step": gemm_b, "ms_per_step": round(gemm_ms, 4),
                              "calls": len(gemm_launches)},

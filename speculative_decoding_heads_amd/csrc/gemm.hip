@@ -402,11 +402,20 @@ __global__ __launch_bounds__(NWV * 64) void gemm_lds_kernel(int M, int N, int K,
   // EPI_QKV_ROPE maps the four 16-row wave tiles to two blocks of the first
   // half of one head's rows and the same blocks of the second half (waves
   // w and w ^ 1 hold the two rotary partners of the same dimensions)
-  const bool rope = NWV == 4 && e.mode == EPI_QKV_ROPE;
+  // With three waves (equal numbers of rotary pairs and V blocks, as in
+  // multi-head attention) waves 0 and 1 hold one pair of q or k blocks and
+  // wave 2 one 16-row block of V, so every workgroup has 48 rows.
+  const bool rope = NR == 1 && (NWV == 4 || NWV == 3) && e.mode == EPI_QKV_ROPE;
   int n0 = (nt * NWV + w) * TN;
   if (rope) {
-    const int wg_per_head = e.Dh / 64, hd = nt / wg_per_head, sub = nt % wg_per_head;
-    n0 = hd * e.Dh + (w & 1) * (e.Dh / 2) + (sub * 2 + (w >> 1)) * 16;
+    if constexpr (NWV == 3) {
+      const int pairs_per_head = e.Dh / 32;
+      n0 = w < 2 ? (nt / pairs_per_head) * e.Dh + w * (e.Dh / 2) + (nt % pairs_per_head) * 16
+                 : (e.Hq + e.Hkv) * e.Dh + nt * 16;
+    } else {
+      const int wg_per_head = e.Dh / 64, hd = nt / wg_per_head, sub = nt % wg_per_head;
+      n0 = hd * e.Dh + (w & 1) * (e.Dh / 2) + (sub * 2 + (w >> 1)) * 16;
+    }
   }
   const int m0 = mt * GM;
   const int nchunks = (K / GK) / U;
@@ -528,9 +537,167 @@ __global__ __launch_bounds__(NWV * 64) void gemm_lds_kernel(int M, int N, int K,
     for (; v + NS + 1 < per; v += NS) seq(full_round, v, std::make_integer_sequence<int, NS>{});
     for (; v < per; v += NS) seq(last_round, v, std::make_integer_sequence<int, NS>{});
   }
-  if constexpr (NR == 1 && NWV == 4) {
+  if constexpr (NR == 1 && (NWV == 4 || NWV == 3)) {
     if (rope) {
       rope_epilogue(acc, lds, w, n0, m0, M, e, l16, lg);
+      return;
+    }
+  }
+  store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
+}
+
+// 16 bytes per lane from sbase + off into LDS at lds + 16 * lane (gfx950
+// global_load_lds_dwordx4; M0 holds the wave-uniform LDS address, one wait
+// state after writing it).  Inline assembly: the compiler's own accounting of
+// these loads would wait for all of them before any LDS read; the kernel waits
+// for them itself (s_waitcnt vmcnt + barrier).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Streaming kernel for M > 32 with a deep ring of LDS chunk buffers.  Same
+// tile ownership and accumulator layout as gemm_lds_kernel (NWV waves, each
+// NR*16 W rows, 64 A rows, 16x16x32 products), but both operands travel
+// global -> LDS by 16-byte direct loads, so the depth of the pipeline is set
+// by the 160 KB of LDS rather than by registers: D chunks of 64 k (one
+// 128-byte line of every W and A row) are in the ring, D - 1 of them in
+// flight.  A product of this shape streams its weights once, and its rate
+// follows the bytes each CU keeps in flight.  Each wave loads its own W rows;
+// the 64 A rows of a chunk are split over the waves; one barrier per chunk
+// makes the chunk visible and frees the buffer read in the previous step.  The
+// 16-byte pieces of a row are permuted by (row / 2) mod 8 so the fragment reads
+// of 16 consecutive rows fall in distinct banks.  Loads past the last chunk
+// re-read it (cache hits, never multiplied), so every step waits for the same
+// count.  grid (N tiles of NWV*NR*16 rows, m tiles * SK, batch).
+template <int NR, int NWV, int D>
+__global__ __launch_bounds__(NWV * 64) void gemm_dma_kernel(int M, int N, int K, const bf16_t* __restrict__ A,
+                                                            int64_t lda, int64_t sA, const bf16_t* __restrict__ W,
+                                                            int64_t sW, int SK, EpiArgs e, int64_t sC, int64_t sR,
+                                                            float* __restrict__ part) {
+  constexpr int MB = 4, TN = NR * 16;
+  constexpr int KC = 2 * GK;               // k per chunk
+  constexpr int ROWB = KC * 2;             // 128 bytes per row and chunk
+  constexpr int AB = GM * ROWB;            // A bytes per chunk
+  constexpr int WWB = TN * ROWB;           // W bytes per wave and chunk
+  constexpr int CB = AB + NWV * WWB;       // one ring slot
+  constexpr int AINS = AB / 1024;          // direct loads per A chunk (8 rows each)
+  constexpr int AQ = (AINS + NWV - 1) / NWV;
+  constexpr int WQ = WWB / 1024;
+  constexpr int IPW = AQ + WQ;             // direct loads per wave and chunk
+  constexpr bool SPARE = AQ * NWV != AINS;  // the surplus A loads land in a spare 1 KB
+  static_assert(D >= 3 && (D - 2) * IPW <= 63, "wait count range");
+  static_assert(D * CB + (SPARE ? 1024 : 0) <= 160 * 1024 && D * CB >= 16384, "LDS size");
+  __shared__ __align__(16) char sm[D * CB + (SPARE ? 1024 : 0)];
+  const int bz = blockIdx.z;
+  const int nt = blockIdx.x;
+  const int mt = blockIdx.y / SK;
+  const int ks = blockIdx.y % SK;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  A += bz * sA;
+  W += bz * sW;
+  const bool rope = NR == 1 && (NWV == 4 || NWV == 3) && e.mode == EPI_QKV_ROPE;
+  int n0 = (nt * NWV + w) * TN;
+  if (rope) {
+    if constexpr (NWV == 3) {
+      const int pairs_per_head = e.Dh / 32;
+      n0 = w < 2 ? (nt / pairs_per_head) * e.Dh + w * (e.Dh / 2) + (nt % pairs_per_head) * 16
+                 : (e.Hq + e.Hkv) * e.Dh + nt * 16;
+    } else {
+      const int wg_per_head = e.Dh / 64, hd = nt / wg_per_head, sub = nt % wg_per_head;
+      n0 = hd * e.Dh + (w & 1) * (e.Dh / 2) + (sub * 2 + (w >> 1)) * 16;
+    }
+  }
+  const int m0 = mt * GM;
+  const int nchunks = K / KC;
+  const int c0 = (int)((int64_t)nchunks * ks / SK), c1 = (int)((int64_t)nchunks * (ks + 1) / SK);
+  const int per = c1 - c0;
+  // rotated k walk (see gemm_lds_kernel); fixed for a shape
+  const int rot = per > 0 ? (int)(((unsigned)nt * 37u) % (unsigned)per) : 0;
+  auto clampc = [&](int x) {
+    int y = min(x, per - 1) + rot;
+    if (y >= per) y -= per;
+    return c0 + y;
+  };
+  auto pslot = [](int r) { return (r >> 1) & 7; };
+
+  // direct-load source offsets (bytes from the chunk's first column): lane
+  // writes LDS row lane / 8 of its instruction, slot lane % 8, which holds
+  // piece slot ^ pslot(row) of that row
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)sm);
+  const int drow = lane >> 3, dslot = lane & 7;
+  uint32_t asrc[AQ], adst[AQ], wsrc[WQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int ins = w + NWV * q;
+    const int r = (ins < AINS ? ins : 0) * 8 + drow;
+    asrc[q] = (uint32_t)((int64_t)min(m0 + r, M - 1) * lda * 2 + ((dslot ^ pslot(r)) * 16));
+    adst[q] = ins < AINS ? (uint32_t)(ins * 1024) : (uint32_t)(D * CB);
+  }
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int r = q * 8 + drow;  // row within this wave's W rows
+    wsrc[q] = (uint32_t)((int64_t)min(n0 + r, N - 1) * K * 2 + ((dslot ^ pslot(r)) * 16));
+  }
+  auto issue = [&](int x, int buf) __attribute__((always_inline)) {
+    const int64_t kb = (int64_t)clampc(x) * ROWB;
+    const char* ab = (const char*)A + kb;
+    const char* wb = (const char*)W + kb;
+    const uint32_t slot = lds0 + buf * CB;
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) dma16(ab, asrc[q], adst[q] < (uint32_t)AB ? slot + adst[q] : lds0 + adst[q]);
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) dma16(wb, wsrc[q], slot + AB + w * WWB + q * 1024);
+  };
+  // fragment read offsets (rows l16 of each 16-row block; pslot depends on l16 only)
+  uint32_t frd[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) frd[s] = (uint32_t)(l16 * ROWB + (((s * 4 + lg) ^ pslot(l16)) * 16));
+
+  f32x4 acc[NR][MB];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (per > 0) {
+#pragma unroll
+    for (int t = 0; t < D - 1; ++t) issue(t, t);
+    int buf = 0;
+    for (int x = 0; x < per; ++x) {
+      // chunk x is complete once at most (D - 2) chunks' loads are outstanding
+      // (vmcnt[3:0] and [15:14]; expcnt and lgkmcnt fields left at no-wait)
+      constexpr int WN = (D - 2) * IPW;
+      __builtin_amdgcn_s_waitcnt((WN & 0xf) | (0x7 << 4) | (0xf << 8) | (((WN >> 4) & 0x3) << 14));
+      __syncthreads();
+      issue(x + D - 1, buf == 0 ? D - 1 : buf - 1);
+      const char* cb = sm + buf * CB;
+      F8 wf[2][NR], af[2][MB];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) wf[s][i].u = *(const uint4*)(cb + AB + w * WWB + i * 16 * ROWB + frd[s]);
+#pragma unroll
+        for (int j = 0; j < MB; ++j) af[s][j].u = *(const uint4*)(cb + j * 16 * ROWB + frd[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s][i].v, af[s][j].v, acc[i][j], 0, 0, 0);
+      buf = buf == D - 1 ? 0 : buf + 1;
+    }
+    // the re-reads past the last chunk land before the LDS is reused or freed
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
+  }
+  if constexpr (NR == 1 && (NWV == 4 || NWV == 3)) {
+    if (rope) {
+      rope_epilogue(acc, sm, w, n0, m0, M, e, l16, lg);
       return;
     }
   }
@@ -570,6 +737,7 @@ struct GemmPlan {
   int NWV;   // gemm_lds_kernel: waves per workgroup (4, or 3 for 96-row tiles)
   bool KW;   // register kernel: the four waves split K
   bool LDS;  // M > 32: A staged in LDS (gemm_lds_kernel)
+  bool DMA;  // M > 32: both operands by direct loads into an LDS ring (gemm_dma_kernel)
   size_t part_bytes;
 };
 
@@ -588,7 +756,9 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
   static const int e_u = env_int("MEDUSA_GEMM_U", 2);       // k-steps per chunk cap (1 | 2 | 4)
   static const int e_waves = env_int("MEDUSA_GEMM_WAVES", 1024);
   static const int e_sk = env_int("MEDUSA_GEMM_SK", 0);     // forced K split (0: from the wave target)
+  static const int e_dma = env_int("MEDUSA_GEMM_DMA", 1);   // M > 32 on gemm_dma_kernel when the shape allows
   GemmPlan p;
+  p.DMA = false;
   const int mrows = M < GM ? M : GM;
   p.MB = mrows <= 16 ? 1 : (mrows <= 32 ? 2 : 4);
   p.m_tiles = (M + GM - 1) / GM;
@@ -635,6 +805,8 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
     const int nchunks = nsteps / p.U;
     const int skmax = nchunks / 4 > 0 ? nchunks / 4 : 1;
     p.SK = sk < 1 ? 1 : (sk > skmax ? skmax : sk);
+    // the direct loads address a row by a 32-bit byte offset from the chunk
+    p.DMA = e_dma && p.U == 2 && (int64_t)N * K * 2 < ((int64_t)1 << 32);
   } else {
     p.NWV = 4;
     p.NR = p.MB == 4 && !e_nr4 ? 2 : 4;
@@ -669,8 +841,32 @@ void gemm_bf16_launch(const GemmPlan& p, int M, int N, int K, const void* A, int
 #define GEMM_LAUNCH_LDS(NRV, UV, NSV, NWVV)                                                                 \
   hipLaunchKernelGGL((gemm_lds_kernel<NRV, UV, NSV, NWVV>), grid, dim3(NWVV * 64), 0, stream, M, N, K,          \
                      (const bf16_t*)A, lda, strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
-  if (p.LDS) {
-    if (p.NWV == 3) {
+#define GEMM_LAUNCH_DMA(NRV, NWVV, DV)                                                                       \
+  hipLaunchKernelGGL((gemm_dma_kernel<NRV, NWVV, DV>), grid, dim3(NWVV * 64), 0, stream, M, N, K,               \
+                     (const bf16_t*)A, lda, strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
+  static const int e_half = env_int("MEDUSA_GEMM_DMA_HALF", 0);  // tuning runs: a ring of about half the depth
+  if (p.LDS && p.DMA && e_half) {
+    if (p.NR == 1) {
+      if (p.NWV == 3) GEMM_LAUNCH_DMA(1, 3, 6);
+      else GEMM_LAUNCH_DMA(1, 4, 5);
+    } else {
+      if (p.NWV == 3) GEMM_LAUNCH_DMA(2, 3, 4);
+      else GEMM_LAUNCH_DMA(2, 4, 4);
+    }
+  } else if (p.LDS && p.DMA) {
+    // ring depth: as many 64-k chunks as fit the LDS
+    if (p.NR == 1) {
+      if (p.NWV == 3) GEMM_LAUNCH_DMA(1, 3, 11);
+      else GEMM_LAUNCH_DMA(1, 4, 9);
+    } else {
+      if (p.NWV == 3) GEMM_LAUNCH_DMA(2, 3, 7);
+      else GEMM_LAUNCH_DMA(2, 4, 6);
+    }
+  } else if (p.LDS) {
+    if (p.NWV == 3 && p.NR == 1) {
+      if (p.U == 2) GEMM_LAUNCH_LDS(1, 2, 4, 3);
+      else GEMM_LAUNCH_LDS(1, 1, 4, 3);
+    } else if (p.NWV == 3) {
       if (p.U == 2) GEMM_LAUNCH_LDS(2, 2, 4, 3);
       else GEMM_LAUNCH_LDS(2, 1, 4, 3);
     } else if (p.NR == 1) {
@@ -700,6 +896,7 @@ void gemm_bf16_launch(const GemmPlan& p, int M, int N, int K, const void* A, int
 #undef GEMM_LAUNCH
 #undef GEMM_LAUNCH_KW
 #undef GEMM_LAUNCH_LDS
+#undef GEMM_LAUNCH_DMA
 }
 
 }  // namespace
@@ -879,6 +1076,15 @@ int gemm_qkv_rope_bf16(int B, int T, int K, int Hq, int Hkv, int Dh, const bf16_
   p.NWV = 4;
   p.SK = 1;
   p.n_tiles = N / 64;
+  // 48-row workgroups (a q or k rotary pair + one V block) when the pairs and
+  // the V blocks come out even and that puts fewer rows on the busiest CU than
+  // 64-row workgroups (MEDUSA_GEMM_QKV3 = 0 keeps 64 rows, for tuning runs)
+  static const int e_qkv3 = env_int("MEDUSA_GEMM_QKV3", 1);
+  const int pairs = (Hq + Hkv) * Dh / 32;
+  if (e_qkv3 && pairs == Hkv * Dh / 16 && (pairs + 255) / 256 * 48 < (p.n_tiles + 255) / 256 * 64) {
+    p.NWV = 3;
+    p.n_tiles = pairs;
+  }
   EpiArgs e{EPI_QKV_ROPE, nullptr, 0, nullptr, 0, A, K, K, 0, pos, cos_t, sin_t, max_pos, T, Hq, Hkv, Dh,
             q_out, k_out, v_out};
   gemm_bf16_launch(p, M, N, K, A, K, 0, W, 0, e, 0, 0, nullptr, 1, stream);

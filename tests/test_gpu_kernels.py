@@ -228,7 +228,9 @@ def test_heads_topk_fp32_small(dev):
                                    (300, 1000, 512), (256, 512, 64), (512, 4096, 4096), (768, 16484, 256),
                                    (1000, 20000, 128), (192, 256, 32), (700, 300, 96),
                                    # streaming path with three-wave 96-row workgroup tiles (ragged last tile)
-                                   (64, 20000, 256)])
+                                   (64, 20000, 256),
+                                   # streaming path, 128-row workgroup tiles; 48 rows (clamped A rows)
+                                   (64, 32000, 256), (48, 5000, 1024)])
 def test_gemm_bf16(dev, M, N, K):
     import torch
     from speculative_decoding_heads_amd import api
