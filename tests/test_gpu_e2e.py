@@ -171,6 +171,50 @@ def test_bf16_forward_vs_oracle(dev, heads_kv_dim):
     assert_close(to_np(Vt), rV, rtol=2e-2, atol=1e-2 * np.abs(rV).max(), what="tree V")
 
 
+def test_bf16_forward_full_width_layer(dev):
+    """One 7B-shaped layer (d 4096, 32 x 128 multi-head attention, SwiGLU 11008) over the 64
+    tree rows of the page's tree at prefix 1024: every projection runs at the launch shape of
+    the verify step with its whole k walk (48-row q/K/V workgroups with the rotary epilogue,
+    96-row gate/up workgroups, the K split of W_o and down, 64-row LM-head tiles), and the
+    attention at 32 multi-head heads with several KV splits."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd.model import Model
+    from workloads import bf16_round
+
+    class Cfg:
+        n_layers = 1
+        d = 4096
+        n_heads, n_kv_heads, head_dim = 32, 32, 128
+        ffn = 11008
+        vocab = 2048
+        n_medusa = 1
+        rope_theta = 10000.0
+        norm_eps = 1e-6
+    say("e2e bf16 full-width layer forward vs oracle")
+    params, heads = tiny_model(11, cfg=Cfg, bf16=True)
+    P, H = _upload(params, heads, torch.bfloat16, dev)
+    model = Model(P, H, max_pos=2048)
+    tree = api.Tree(PAGE_TREE_CHOICES)
+    ot = tree_buffers(PAGE_TREE_CHOICES)
+    rng = np.random.default_rng(12)
+    B, L, Lmax = 1, 1024, 1088
+    Kc = bf16_round(rng.standard_normal((1, B, 32, Lmax, 128)).astype(np.float32))
+    Vc = bf16_round(rng.standard_normal((1, B, 32, Lmax, 128)).astype(np.float32))
+    seq = np.array([L], np.int32)
+    toks = rng.integers(0, Cfg.vocab, (B, 64)).astype(np.int32)
+    pos = (seq[:, None] + ot["depth"][None, :]).astype(np.int32)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    logits, h, Kt, Vt = model.forward(d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev), to_dev(Vc, torch.bfloat16, dev),
+                                      d(seq), tree, L_hint=Lmax)
+    torch.cuda.synchronize()
+    rl, rh, rK, rV = oracle_forward(params, toks, pos, Kc, Vc, seq, ot["anc"], bf16=True)
+    assert_close(to_np(Kt), rK, rtol=2e-2, atol=1e-2 * np.abs(rK).max(), what="tree K")
+    assert_close(to_np(Vt), rV, rtol=2e-2, atol=1e-2 * np.abs(rV).max(), what="tree V")
+    assert_close(to_np(h), rh, rtol=2e-2, atol=1e-2 * np.abs(rh).max(), what="h")
+    assert_close(to_np(logits), rl, rtol=2e-2, atol=1e-2 * max(np.abs(rl).max(), 1.0), what="logits")
+
+
 @pytest.mark.parametrize("mode", [GREEDY, TYPICAL])
 def test_bf16_step_acceptance_on_identical_logits(dev, mode):
     """The step's decisions equal the oracle's rule applied to the same forward's logits."""
