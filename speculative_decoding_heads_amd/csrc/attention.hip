@@ -104,47 +104,75 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
 
 constexpr int ATTN_MAX_SPLITS = 64;
 
-// grid (R, Hkv, B), block Dh threads: merge the split partials of one query row.
-// The split maxima and sums go through shared memory in one round trip, then
-// each thread adds its dimension over the splits with independent loads.
+// grid (ceil(R / 2), Hkv, B), block 64 threads: merge the split partials of
+// two query rows, one half-wave a row, four dimensions a lane (16-byte
+// loads).  Lane s of a half reads split s's maximum and sum (and s + 32's), the
+// half-wave reduces them with cross-lane swaps, and each split's weight is
+// then broadcast from its lane while the partial rows are added in split
+// order.  Dh % 4 == 0, Dh <= 128, n_splits <= 64.
 template <typename T>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ ws_o,
-                                                           const float* __restrict__ ws_ml, int Tn, int Hq, int Hkv,
-                                                           int Dh, int n_splits, T* __restrict__ out) {
-  __shared__ float sm[ATTN_MAX_SPLITS], sl[ATTN_MAX_SPLITS];
-  const int r = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ ws_o,
+                                                          const float* __restrict__ ws_ml, int Tn, int Hq, int Hkv,
+                                                          int Dh, int n_splits, T* __restrict__ out) {
   const int G = Hq / Hkv;
   const int R = Tn * G;
+  const int lane = threadIdx.x & 31;
+  const int r = blockIdx.x * 2 + (threadIdx.x >> 5);
+  const bool valid = r < R;
+  const int rr = valid ? r : R - 1;  // a half past the rows works on the last row and stores nothing
+  const int kvh = blockIdx.y, b = blockIdx.z;
   const size_t slab = (size_t)b * Hkv + kvh;
-  const size_t base = slab * n_splits * (size_t)R + r;  // partial row of split s: base + s * R
-  for (int s = threadIdx.x; s < n_splits; s += blockDim.x) {
-    sm[s] = ws_ml[(base + (size_t)s * R) * 2];
-    sl[s] = ws_ml[(base + (size_t)s * R) * 2 + 1];
+  const size_t base = slab * n_splits * (size_t)R + rr;  // partial row of split s: base + s * R
+  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+  if (lane < n_splits) {
+    m0 = ws_ml[(base + (size_t)lane * R) * 2];
+    l0 = ws_ml[(base + (size_t)lane * R) * 2 + 1];
   }
-  __syncthreads();
-  float mt = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mt = fmaxf(mt, sm[s]);
-  float lt = 0.f;
-  for (int s = 0; s < n_splits; ++s)
-    if (sm[s] != -INFINITY) lt += sl[s] * __builtin_amdgcn_exp2f(sm[s] - mt);
+  if (lane + 32 < n_splits) {
+    m1 = ws_ml[(base + (size_t)(lane + 32) * R) * 2];
+    l1 = ws_ml[(base + (size_t)(lane + 32) * R) * 2 + 1];
+  }
+  float mt = fmaxf(m0, m1);
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 32));
+  const float w0 = m0 != -INFINITY ? __builtin_amdgcn_exp2f(m0 - mt) : 0.f;
+  const float w1 = m1 != -INFINITY ? __builtin_amdgcn_exp2f(m1 - mt) : 0.f;
+  float lt = l0 * w0 + l1 * w1;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) lt += __shfl_xor(lt, o, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const int d0 = lane * 4 < Dh ? lane * 4 : 0;  // lanes past Dh load a valid column and store nothing
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= n_splits; s += 4) {
+    float4 v[4];
+    float w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = *(const float4*)(ws_o + (base + (size_t)(s + u) * R) * Dh + d0);
+      w[u] = __shfl(s + u < 32 ? w0 : w1, (s + u) & 31, 32);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[0] += v[u].x * w[u];
+      acc[1] += v[u].y * w[u];
+      acc[2] += v[u].z * w[u];
+      acc[3] += v[u].w * w[u];
+    }
+  }
+  for (; s < n_splits; ++s) {
+    const float4 v = *(const float4*)(ws_o + (base + (size_t)s * R) * Dh + d0);
+    const float w = __shfl(s < 32 ? w0 : w1, s & 31, 32);
+    acc[0] += v.x * w;
+    acc[1] += v.y * w;
+    acc[2] += v.z * w;
+    acc[3] += v.w * w;
+  }
+  if (!valid || lane * 4 >= Dh) return;
   const int node = r / G, g = r % G;
   const size_t ooff = (((size_t)b * Tn + node) * Hq + (size_t)kvh * G + g) * Dh;
-  for (int d = threadIdx.x; d < Dh; d += blockDim.x) {
-    float acc = 0.f;
-    int s = 0;
-    for (; s + 4 <= n_splits; s += 4) {
-      float v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = ws_o[(base + (size_t)(s + u) * R) * Dh + d];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (sm[s + u] != -INFINITY) acc += v[u] * __builtin_amdgcn_exp2f(sm[s + u] - mt);
-    }
-    for (; s < n_splits; ++s)
-      if (sm[s] != -INFINITY) acc += ws_o[(base + (size_t)s * R) * Dh + d] * __builtin_amdgcn_exp2f(sm[s] - mt);
-    Elem<T>::store(out, ooff + d, acc * inv);
-  }
+  for (int i = 0; i < 4; ++i) Elem<T>::store(out, ooff + d0 + i, acc[i] * inv);
 }
 
 struct MfmaPlan {
@@ -219,8 +247,8 @@ extern "C" int tree_attention(int dtype, int B, int T, int Hq, int Hkv, int Dh, 
                                 (bf16_t*)out, ws_o, ws_ml);
     if (rc) return rc;
     if (p.n_splits > 1) {
-      hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(T * (Hq / Hkv), Hkv, B), dim3(Dh), 0, stream, ws_o, ws_ml,
-                         T, Hq, Hkv, Dh, p.n_splits, (bf16_t*)out);
+      hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3((T * (Hq / Hkv) + 1) / 2, Hkv, B), dim3(64), 0, stream,
+                         ws_o, ws_ml, T, Hq, Hkv, Dh, p.n_splits, (bf16_t*)out);
       return check_launch("tree_attention combine");
     }
     return MEDUSA_OK;
