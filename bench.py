@@ -15,7 +15,8 @@ Also measured (same JSON line):
                  32 layers' weights, against 8 TB/s; `traffic` from the committed
                  rocprofv3 FETCH_SIZE / WRITE_SIZE summary when the kernel source still
                  matches it.  `step_projections` adds every projection of one step.
-  tree_attention the attention kernel alone at batch 8, 32/8 heads, prefix 65536, and
+  tree_attention the attention kernel alone at batch 8, 32/8 heads, prefix 65536, at
+                 batch 1 with the 7B-shaped model's 32 heads (no KV sharing), prefix 65536, and
                  at batch 1, prefix 1024, against 8 TB/s
   prefix_sweep   the same step (eager launches) at prefixes 4k, 16k and 64k, the cache
                  filled with N(0,1) keys and values (5 timed steps each)
@@ -352,8 +353,7 @@ def main():
     log("projections of one step: %.3f ms, %.1f GB/s" % (gemm_ms, gemm_gbs))
 
     # ---- tree attention alone
-    def attn_case(Bc, L, reps):
-        Hkv = 8
+    def attn_case(Bc, L, reps, Hkv=8):
         q = torch_normal((Bc, T, 32, Dh), 1.0, 11, dev, torch.bfloat16)
         # rotate over > 1 GB of distinct K/V at small L so the 256 MB last-level cache cannot serve them
         nbuf = max(1, min(128, int(1.2e9 // (Bc * Hkv * L * Dh * 2 * 2)) + 1))
@@ -380,10 +380,13 @@ def main():
 
     a64_ms, a64_b = attn_case(8, 65536, args.attn_reps)
     a1k_ms, a1k_b = attn_case(1, 1024, args.attn_reps * 5)
+    # the 7B-shaped model's attention (32 heads, no KV-head sharing) at a long prefix
+    amha_ms, amha_b = attn_case(1, 65536, args.attn_reps, Hkv=32)
+    amha_gbs = amha_b / (amha_ms * 1e-3) / 1e9
     a64_gbs = a64_b / (a64_ms * 1e-3) / 1e9
     a1k_gbs = a1k_b / (a1k_ms * 1e-3) / 1e9
-    log("tree_attention B8 L65536: %.1f us, %.1f GB/s; B1 L1024: %.1f us, %.1f GB/s" %
-        (a64_ms * 1e3, a64_gbs, a1k_ms * 1e3, a1k_gbs))
+    log("tree_attention B8 L65536: %.1f us, %.1f GB/s; B1 L1024: %.1f us, %.1f GB/s; 32 MHA heads L65536: %.1f us, "
+        "%.1f GB/s" % (a64_ms * 1e3, a64_gbs, a1k_ms * 1e3, a1k_gbs, amha_ms * 1e3, amha_gbs))
 
     # ---- the Medusa heads on every node of 8 sequences' trees (M = 8 * 64 = 512 hidden
     # states): the heads' products in the compute-bound regime (square-tile kernel)
@@ -443,7 +446,9 @@ def main():
             "B8_L65536": {"us": round(a64_ms * 1e3, 2), "achieved": round(a64_gbs, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": round(a64_gbs / HBM_PEAK_GBS, 4), "bytes": a64_b},
             "B1_L1024": {"us": round(a1k_ms * 1e3, 2), "achieved": round(a1k_gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(a1k_gbs / HBM_PEAK_GBS, 4), "bytes": a1k_b}},
+                         "unit": "GB/s", "frac": round(a1k_gbs / HBM_PEAK_GBS, 4), "bytes": a1k_b},
+            "B1_MHA32_L65536": {"us": round(amha_ms * 1e3, 2), "achieved": round(amha_gbs, 1), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(amha_gbs / HBM_PEAK_GBS, 4), "bytes": amha_b}},
         "prefix_sweep": sweep,
         "heads_all_tree_nodes": {
             "kernels": "gemm_tile_kernel (W1 with the SiLU residual, W2 to fp32 logits) + top-K",

@@ -11,7 +11,9 @@
 //    each wave a (BM/2) x 64 block of v_mfma_f32_32x32x16_bf16 accumulators;
 //    BM = 256, or 128 when 256-row tiles would leave most CUs idle;
 //  * A and W chunks of 64 k go straight from global memory into LDS (16-byte
-//    direct loads, global_load_lds_dwordx4), two chunks deep; a chunk holds a
+//    direct loads, global_load_lds_dwordx4), two chunks deep for 256-row
+//    tiles (128 KB of LDS) and three for 128-row tiles (144 KB: a third buffer
+//    runs a product whose weights come from HBM 20% faster); a chunk holds a
 //    whole 128-byte line of each row (chunks of 32 k fetched each line twice
 //    through the vector L1 and ran 15-20% slower), the row's eight 16-byte
 //    pieces permuted by a function of the row so the fragment reads of
@@ -334,8 +336,8 @@ int gemm_tile_bf16(int M, int N, int K, const bf16_t* A, int64_t lda, int64_t st
   const int64_t ncu = cu_count();
   const int64_t rounds256 = (tiles256 + ncu - 1) / ncu, rounds128 = (tiles128 + ncu - 1) / ncu;
   const bool bm256 = rounds128 * 7 >= rounds256 * 10;
-  // k chunk of 64 (whole 128-byte lines of each row, two buffers) or of 32
-  // (half lines, four buffers)
+  // k chunk of 64 (whole 128-byte lines of each row; two buffers at 256 rows,
+  // three at 128) or of 32 (half lines, four buffers)
   static const bool kc32 = getenv("MEDUSA_TILE_KC") && atoi(getenv("MEDUSA_TILE_KC")) == 32;
   static const int bm_env = getenv("MEDUSA_TILE_BM") ? atoi(getenv("MEDUSA_TILE_BM")) : 0;
   if (bm_env == 256 || (bm_env != 128 && bm256)) {
@@ -346,8 +348,13 @@ int gemm_tile_bf16(int M, int N, int K, const bf16_t* A, int64_t lda, int64_t st
       hipLaunchKernelGGL((gemm_tile_kernel<256, 64, 2>), dim3((unsigned)tiles256), dim3(TTHR), 0, stream, M, N, K, A,
                          lda, strideA, W, strideW, e);
   } else {
+    // three chunk buffers (MEDUSA_TILE_NS3 = 0: two, for tuning runs)
+    static const bool ns3 = !(getenv("MEDUSA_TILE_NS3") && atoi(getenv("MEDUSA_TILE_NS3")) == 0);
     if (kc32)
       hipLaunchKernelGGL((gemm_tile_kernel<128, 32, 4>), dim3((unsigned)tiles128), dim3(TTHR), 0, stream, M, N, K, A,
+                         lda, strideA, W, strideW, e);
+    else if (ns3)
+      hipLaunchKernelGGL((gemm_tile_kernel<128, 64, 3>), dim3((unsigned)tiles128), dim3(TTHR), 0, stream, M, N, K, A,
                          lda, strideA, W, strideW, e);
     else
       hipLaunchKernelGGL((gemm_tile_kernel<128, 64, 2>), dim3((unsigned)tiles128), dim3(TTHR), 0, stream, M, N, K, A,
