@@ -826,9 +826,12 @@ GemmPlan gemm_plan(int M, int N, int K, int batch) {
 }
 
 // Launch the bf16 product kernel of plan p (partials, when left, go to ws).
-void gemm_bf16_launch(const GemmPlan& p, int M, int N, int K, const void* A, int64_t lda, int64_t strideA,
+void gemm_bf16_launch(const GemmPlan& p0, int M, int N, int K, const void* A, int64_t lda, int64_t strideA,
                       const void* W, int64_t strideW, const EpiArgs& e, int64_t strideC, int64_t strideR, void* ws,
                       int batch, hipStream_t stream) {
+  // the direct loads address an activation row by a 32-bit byte offset too
+  GemmPlan p = p0;
+  if (p.DMA && (int64_t)M * lda * 2 >= ((int64_t)1 << 32)) p.DMA = false;
   dim3 grid(p.n_tiles, p.m_tiles * p.SK, batch);
 #define GEMM_LAUNCH_KW(MBV, NRV, UV, KWV)                                                                      \
   hipLaunchKernelGGL((gemm_bf16_kernel<MBV, NRV, UV, KWV>), grid, dim3(GTHR), 0, stream, M, N, K, (const bf16_t*)A, \
