@@ -165,7 +165,8 @@ def main():
 
     from speculative_decoding_heads_amd import api
     from speculative_decoding_heads_amd._lib import EPI_F32, EPI_RESID, EPI_SWIGLU, TYPICAL, lib
-    from speculative_decoding_heads_amd.model import Model, State, StepGraph, prefill, step, step_workspace_size
+    from speculative_decoding_heads_amd.model import (Model, State, StepGraph, init_topk_carry, prefill, step,
+                                                      step_fused, step_fused_workspace_size, step_workspace_size)
     from workloads import SevenBConfig, model_weights_torch, prompt_tokens, seeded_tree_choices, torch_normal
 
     dev = torch.device("cuda:0")
@@ -262,6 +263,27 @@ def main():
     assert int(st.err[0]) == 0, "state error flag set"
     mean_tokens = float(acc_sum.sum()) / (args.steps * B) + 1.0
     steps_per_s = 1e3 / step_ms
+
+    # fused draft + verify: the heads on all 64 tree nodes inside the step, the
+    # next candidates taken at the selected node (eager launches, same prefix reset)
+    fws = torch.empty(step_fused_workspace_size(model, tree, B, Lmax), dtype=torch.uint8, device=dev)
+    carry = init_topk_carry(model, tree, st)
+
+    def fused_step():
+        st.seq_len.copy_(base_seq)
+        st.n_out.zero_()
+        step_fused(model, tree, st, carry, TYPICAL, tau, eps, delta, L_hint=Lmax, ws=fws)
+
+    for _ in range(args.warmup):
+        fused_step()
+    torch.cuda.synchronize()
+    with Timer() as tf:
+        for _ in range(args.steps):
+            fused_step()
+    fused_ms = tf.ms() / args.steps
+    assert int(st.err[0]) == 0, "state error flag set"
+    log("fused draft+verify step %.3f ms" % fused_ms)
+    del fws
     log("step %.3f ms (wall %.3f ms), %.1f steps/s, mean tokens/step %.2f" % (step_ms, wall_ms, steps_per_s,
                                                                               mean_tokens))
 
@@ -450,6 +472,9 @@ def main():
             "B1_MHA32_L65536": {"us": round(amha_ms * 1e3, 2), "achieved": round(amha_gbs, 1), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(amha_gbs / HBM_PEAK_GBS, 4), "bytes": amha_b}},
         "prefix_sweep": sweep,
+        "fused_draft_verify": {"ms_per_step": round(fused_ms, 4), "steps_per_s": round(1e3 / fused_ms, 3),
+                               "note": "heads on all 64 tree nodes in the step (M = 64), next candidates at the "
+                                       "selected node; the reported step runs the heads on the selected node only"},
         "heads_all_tree_nodes": {
             "kernels": "gemm_tile_kernel (W1 with the SiLU residual, W2 to fp32 logits) + top-K",
             "rows": Bh, "bound": "mfma", "us": round(heads_ms * 1e3, 2), "achieved": round(heads_tfs, 1),

@@ -176,6 +176,27 @@ int medusa_step(const medusa_model* m, const medusa_tree* t, int B, int mode, fl
                 size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Fused draft + verify (page "大模型推理 memory bandwidth bound (5) - Medusa",
+ * sections 二.5 and 二.7: the Medusa heads run on every tree position in the
+ * verify pass, and the next candidates are taken at the accepted position,
+ * medusa_logits[:, best, accept_length]).  One step: candidates from
+ * topk_carry [B, H, K] int32 (device, caller-owned; in: this step's per-head
+ * top-K, e.g. medusa_heads_topk on h_sel after prefill), the verify forward,
+ * the heads and their top-K on all B*T tree nodes' final hidden states,
+ * acceptance, KV compaction, and out: topk_carry = the top-K at each sequence's
+ * selected node.  The state is updated as by medusa_step (h_sel included), so
+ * both kinds of step can follow each other.  Same tokens as medusa_step under
+ * greedy acceptance (both equal plain greedy decoding); the candidates can
+ * differ from medusa_step's where the heads' products at B*T rows and at B rows
+ * round differently.  Workspace: medusa_step_fused_workspace_size.  Errors as
+ * medusa_step.
+ */
+size_t medusa_step_fused_workspace_size(const medusa_model* m, const medusa_tree* t, int B, int64_t L_hint);
+int medusa_step_fused(const medusa_model* m, const medusa_tree* t, int B, int mode, float temperature, float eps,
+                      float delta, medusa_state* st, int32_t* topk_carry, int64_t L_hint, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/*
  * The same step captured once into a HIP graph (all arguments, including the
  * state and workspace pointers, are baked in); medusa_graph_launch replays it on
  * any stream.  Capture needs a non-default stream.  Replays of one graph must not

@@ -28,7 +28,7 @@ EXPORTED = [
     "medusa_topk_rows",
     "medusa_forward_workspace_size", "medusa_forward", "medusa_prefill_workspace_size", "medusa_prefill",
     "medusa_step_workspace_size", "medusa_step", "medusa_step_graph_create", "medusa_graph_launch",
-    "medusa_graph_destroy",
+    "medusa_graph_destroy", "medusa_step_fused_workspace_size", "medusa_step_fused",
 ]
 
 
@@ -107,6 +107,9 @@ def _declare(lib):
                              _P]),
         "medusa_step_graph_create": (_I, [C.POINTER(ModelDesc), _P, _I, _I, _F, _F, _F, C.POINTER(StateDesc), _L,
                                           _P, _P, _S, _P, C.POINTER(_P)]),
+        "medusa_step_fused_workspace_size": (_S, [C.POINTER(ModelDesc), _P, _I, _L]),
+        "medusa_step_fused": (_I, [C.POINTER(ModelDesc), _P, _I, _I, _F, _F, _F, C.POINTER(StateDesc), _P, _L, _P,
+                                   _S, _P]),
         "medusa_graph_launch": (_I, [_P, _P]),
         "medusa_graph_destroy": (_I, [_P]),
     }

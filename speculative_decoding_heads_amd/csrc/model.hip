@@ -346,6 +346,90 @@ extern "C" int medusa_step(const medusa_model* m, const medusa_tree* t, int B, i
 }
 
 // ---------------------------------------------------------------------------
+// fused draft + verify: the heads on every tree node inside the step
+// ---------------------------------------------------------------------------
+namespace {
+
+// carry[b] = all[b * T + sel[b]]: the H*K top-K entries of the node each
+// sequence's accepted path ends at (sel clamped to [0, T))
+__global__ void gather_topk_kernel(int T, int HK, const int32_t* __restrict__ all, const int32_t* __restrict__ sel,
+                                   int32_t* __restrict__ carry) {
+  const int b = blockIdx.x;
+  int s = sel[b];
+  s = s < 0 ? 0 : (s >= T ? T - 1 : s);
+  for (int i = threadIdx.x; i < HK; i += blockDim.x) carry[(size_t)b * HK + i] = all[((size_t)b * T + s) * HK + i];
+}
+
+struct FusedBufs {
+  int32_t* topk_all;
+  void* hws;
+  size_t hws_bytes;
+  void* step_ws;
+  size_t step_bytes;
+};
+
+size_t fused_layout(const medusa_model* m, const medusa_tree* t, int B, int64_t L_hint, void* ws, FusedBufs* fb) {
+  const int T = t->host.T, K = t->host.K, H = m->n_medusa;
+  Carver c(ws);
+  FusedBufs f;
+  f.topk_all = (int32_t*)c.take((size_t)B * T * H * K * 4);
+  f.hws_bytes = medusa_heads_topk_workspace_size(m->dtype, B * T, m->d, m->vocab, H, K);
+  f.hws = c.take(f.hws_bytes);
+  f.step_bytes = step_layout(m, t, B, L_hint, nullptr, nullptr);
+  f.step_ws = c.take(f.step_bytes);
+  if (fb) *fb = f;
+  return c.off;
+}
+
+}  // namespace
+
+extern "C" size_t medusa_step_fused_workspace_size(const medusa_model* m, const medusa_tree* t, int B,
+                                                   int64_t L_hint) {
+  if (!m || !t || B <= 0 || m->n_medusa <= 0) return 0;
+  return fused_layout(m, t, B, L_hint, nullptr, nullptr);
+}
+
+extern "C" int medusa_step_fused(const medusa_model* m, const medusa_tree* t, int B, int mode, float temperature,
+                                 float eps, float delta, medusa_state* st, int32_t* topk_carry, int64_t L_hint,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_model(m);
+  if (rc) return rc;
+  MEDUSA_REQUIRE(t && st && B >= 1 && topk_carry, MEDUSA_ERR_ARG, "step_fused: bad arguments");
+  MEDUSA_REQUIRE(m->n_medusa >= t->host.D && m->medusa_w1 && m->medusa_w2, MEDUSA_ERR_ARG,
+                 "step_fused: the model has %d Medusa heads, the tree needs %d", m->n_medusa, t->host.D);
+  MEDUSA_REQUIRE(L_hint >= 0 && L_hint <= st->Lmax, MEDUSA_ERR_ARG, "step_fused: L_hint outside [0, Lmax]");
+  MEDUSA_REQUIRE(st->best && st->accept_len && st->sel_node && st->h_sel && st->root && st->seq_len, MEDUSA_ERR_ARG,
+                 "step_fused: null state buffer");
+  FusedBufs f;
+  const size_t need = fused_layout(m, t, B, L_hint, ws, &f);
+  MEDUSA_REQUIRE(ws && ws_bytes >= need, MEDUSA_ERR_WORKSPACE, "step_fused: workspace %zu < %zu", ws_bytes, need);
+  StepBufs s;
+  step_layout(m, t, B, L_hint, f.step_ws, &s);
+  const int H = m->n_medusa, K = t->host.K, T = t->host.T;
+#define CK(x)          \
+  do {                 \
+    int r_ = (x);      \
+    if (r_) return r_; \
+  } while (0)
+  // this step's candidates: the top-K the previous step kept at its selected node
+  CK(tree_build_candidates(t, B, H, K, st->root, topk_carry, st->seq_len, s.tok, s.pos, s.cart, stream));
+  CK(medusa_forward(m, B, T, s.tok, s.pos, st->Kc, st->Vc, st->Lmax, L_hint, st->seq_len, s.Kt, s.Vt, t->dev->anc,
+                    s.logits, s.h, s.fws, s.fws_bytes, stream));
+  // the heads on the final hidden state of every tree node (B*T rows)
+  CK(medusa_heads_topk(m->dtype, B * T, m->d, m->vocab, H, K, s.h, m->medusa_w1, m->medusa_w2, f.topk_all, nullptr,
+                       f.hws, f.hws_bytes, stream));
+  CK(evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best, st->accept_len,
+                        st->sel_node, st->root, s.pws, s.pws_bytes, stream));
+  CK(kv_compact(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, s.Kt, s.Vt,
+                st->best, st->accept_len, st->seq_len, s.tok, st->out_tokens, st->max_new, st->n_out, st->err, stream));
+  CK(medusa_gather_rows(m->dtype, B, T, m->d, s.h, st->sel_node, st->h_sel, stream));
+  hipLaunchKernelGGL(gather_topk_kernel, dim3(B), dim3(64), 0, stream, T, H * K, f.topk_all, st->sel_node,
+                     topk_carry);
+  return check_launch("step_fused carry");
+#undef CK
+}
+
+// ---------------------------------------------------------------------------
 // the step as a HIP graph: one launch replays the ~400 kernels of a step
 // ---------------------------------------------------------------------------
 struct medusa_graph {

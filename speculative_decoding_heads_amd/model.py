@@ -170,3 +170,27 @@ def step(model, tree, state, mode, temperature=0.0, eps=0.09, delta=0.3, L_hint=
     check(lib().medusa_step(C.byref(model.desc), tree.handle, B, int(mode), float(temperature), float(eps),
                             float(delta), C.byref(state.desc), L_hint, ptr(topk_override), ptr(ws), ws.numel(),
                             stream_ptr()))
+
+
+def step_fused_workspace_size(model, tree, B, L_hint):
+    return lib().medusa_step_fused_workspace_size(C.byref(model.desc), tree.handle, B, int(L_hint))
+
+
+def init_topk_carry(model, tree, state):
+    """The first fused step's candidates: the heads' top-K on h_sel (after prefill or a plain step)."""
+    from . import api
+    idx, _ = api.medusa_heads_topk(state.h_sel, model.W1, model.W2, tree.K)
+    return idx
+
+
+def step_fused(model, tree, state, topk_carry, mode, temperature=0.0, eps=0.09, delta=0.3, L_hint=None, ws=None):
+    """medusa_step_fused: heads on every tree node in the step; topk_carry [B, H, K] int32 in and out."""
+    B = state.B
+    L_hint = state.Lmax if L_hint is None else int(L_hint)
+    if tuple(topk_carry.shape) != (B, model.H, tree.K) or str(topk_carry.dtype) != "torch.int32":
+        raise L.MedusaError("step_fused: topk_carry must be int32 [B, H, K]")
+    ws = L._ws(ws, step_fused_workspace_size(model, tree, B, L_hint), state.Kc.device)
+    check(lib().medusa_step_fused(C.byref(model.desc), tree.handle, B, int(mode), float(temperature), float(eps),
+                                  float(delta), C.byref(state.desc), ptr(topk_carry), L_hint, ptr(ws), ws.numel(),
+                                  stream_ptr()))
+

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from oracle.decoder import forward as oracle_forward, greedy_decode, prefill as oracle_prefill
+from oracle.heads import medusa_heads_logits, topk_desc
 from oracle.loop import medusa_generate
 from oracle.posterior import GREEDY, TYPICAL, evaluate_posterior_one
 from oracle.tree import tree_buffers
@@ -70,6 +71,40 @@ def test_tiny_fp32_medusa_equals_plain_greedy(dev):
         assert med[b] == plain[b][: len(med[b])], "GPU medusa != GPU plain greedy"
         assert plain[b] == ref[b, : len(plain[b])].tolist(), "GPU plain greedy != oracle"
         assert med[b] == omed[b], "GPU medusa != oracle medusa"
+
+
+def test_tiny_fp32_fused_draft_verify(dev):
+    """Heads on every tree node inside the step, the next candidates taken at the
+    selected node: greedy tokens and per-step accepted lengths equal the oracle's
+    Medusa loop (heads on the selected node's hidden state; identical per row in
+    float64) and plain greedy decoding."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd.model import Model, State, init_topk_carry, prefill, step_fused
+    say("e2e tiny fp32 fused draft+verify")
+    params, heads = tiny_model(0)
+    prompt = prompt_tokens(100, 2, TinyConfig.prompt_len, TinyConfig.vocab)
+    P, H = _upload(params, heads, torch.float32, dev)
+    model = Model(P, H, max_pos=1024)
+    tree = api.Tree(TWO_HEAD_CHOICES)
+    st = State(model, 2, 256, 128)
+    prefill(model, st, torch.from_numpy(prompt.astype(np.int32)).to(dev))
+    carry = init_topk_carry(model, tree, st)
+    acc = []
+    for _ in range(TinyConfig.n_steps):
+        step_fused(model, tree, st, carry, GREEDY, L_hint=256)
+        acc.append(to_np(st.accept_len).copy())
+    torch.cuda.synchronize()
+    assert int(to_np(st.err)[0]) == 0
+    n, toks = to_np(st.n_out), to_np(st.out_tokens)
+    omed, orecs = medusa_generate(params, heads, tree_buffers(TWO_HEAD_CHOICES), prompt, TinyConfig.n_steps, 256,
+                                  GREEDY)
+    ref = greedy_decode(params, prompt, max(int(x) for x in n), 256)
+    for b in range(2):
+        got = toks[b, : n[b]].tolist()
+        assert got == omed[b], "fused GPU medusa != oracle medusa"
+        assert got == ref[b, : len(got)].tolist(), "fused GPU medusa != plain greedy"
+        assert [int(a[b]) for a in acc] == [int(r["accept_len"][b]) for r in orecs]
 
 
 @pytest.mark.parametrize("ranks", [(0, 0), (1, 2), (1, None)])
@@ -258,6 +293,44 @@ def test_bf16_step_acceptance_on_identical_logits(dev, mode):
         assert torch.equal(st.Vc[:, b, :, s0:s0 + a + 1], Vt[:, b][:, :, rows])
         assert int(to_np(st.seq_len)[b]) == s0 + a + 1
         assert torch.equal(st.h_sel[b], h[b, int(to_np(st.sel_node)[b])])
+
+
+def test_bf16_fused_step_carry_and_state(dev):
+    """A bf16 fused step (heads on all 128 tree nodes of 2 sequences, page tree,
+    typical acceptance) leaves the same state as medusa_step run on the same
+    candidates (acceptance, compaction, h_sel, next root: bit-exact), and a carried
+    top-K that is the oracle's top-K of the heads at the selected node's hidden
+    state, rank by rank, up to bf16-level near-ties."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd.model import Model, State, init_topk_carry, prefill, step, step_fused
+    say("e2e bf16 fused step")
+    (params, heads), Cfg = _small_bf16_model(5)
+    P, H = _upload(params, heads, torch.bfloat16, dev)
+    model = Model(P, H, max_pos=1024)
+    tree = api.Tree(PAGE_TREE_CHOICES)
+    B, Lmax = 2, 256
+    prompt = torch.from_numpy(prompt_tokens(9, B, 70, Cfg.vocab).astype(np.int32)).to(dev)
+    fused, plain = State(model, B, Lmax, 64), State(model, B, Lmax, 64)
+    prefill(model, fused, prompt)
+    prefill(model, plain, prompt)
+    carry = init_topk_carry(model, tree, fused)
+    start = carry.clone()
+    step_fused(model, tree, fused, carry, TYPICAL, 0.7, 0.09, 0.3, L_hint=Lmax)
+    step(model, tree, plain, TYPICAL, 0.7, 0.09, 0.3, L_hint=Lmax, topk_override=start)
+    torch.cuda.synchronize()
+    for name in ("seq_len", "root", "n_out", "out_tokens", "best", "accept_len", "sel_node", "h_sel", "Kc", "Vc"):
+        assert torch.equal(getattr(fused, name), getattr(plain, name)), name
+    ref = medusa_heads_logits(to_np(fused.h_sel).astype(np.float64), heads["W1"], heads["W2"], bf16=True)
+    gi = to_np(carry)
+    K = tree.K
+    for b in range(B):
+        for k in range(ref.shape[1]):
+            rl = ref[b, k]
+            ri = topk_desc(rl, K)
+            assert len(set(gi[b, k].tolist())) == K
+            tol = 1e-2 * np.abs(rl).max()
+            assert np.all(np.abs(rl[gi[b, k]] - rl[ri]) <= tol), (b, k)
 
 
 def test_step_graph_replays_match_eager(dev):
