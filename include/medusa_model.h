@@ -150,6 +150,16 @@ typedef struct medusa_state {
   int32_t* best;
   int32_t* accept_len;
   int32_t* sel_node;
+  /* Per-sequence stop (nullable; the page's generation loop ends at the end-of-
+   * sequence token, section 二.1).  With done [B] set, a step appends each
+   * sequence's accepted tokens up to and including the first stop_token (< 0:
+   * none) and within its output room (max_new - n_out) and cache room
+   * (Lmax - seq_len); done[b] becomes 1 when it appends the stop token or fills
+   * a room, and a sequence with done[b] = 1 appends nothing and keeps its cache
+   * and length.  Prefill resets done to 0.  With done null, a step appends all
+   * a+1 tokens and a full output or cache sets err instead. */
+  int32_t* done;
+  int32_t stop_token;
 } medusa_state;
 
 /*

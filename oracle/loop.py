@@ -5,7 +5,10 @@ Follows "大模型推理 memory bandwidth bound (5) - Medusa", section 二.1
 token and the Medusa-head inputs), then repeat {generate candidates, tree
 decoding, evaluate posterior, update inputs}.  The loop here runs a fixed number
 of steps (no tokenizer or end-of-sequence token in a synthetic run) and works on
-a batch of independent sequences sharing the tree.
+a batch of independent sequences sharing the tree.  With ``stop_token`` (and/or
+``max_new``) each sequence stops on its own: it appends up to and including the
+first stop token, or until its output or cache room is used, and then appends
+nothing more (``update.appended_counts``).
 
 ``topk_hook(step, topk_idx, produced) -> topk_idx`` lets a test replace the
 heads' top-K before candidates are built (forced-acceptance tests); ``produced``
@@ -19,17 +22,18 @@ from .candidates import build_candidates
 from .decoder import forward, prefill
 from .heads import medusa_heads_topk, root_token
 from .posterior import evaluate_posterior
-from .update import accepted_tokens, kv_compact
+from .update import accepted_tokens, appended_counts, kv_compact, kv_compact_counts
 
 
 def medusa_generate(params, heads, tree, prompt, n_steps, Lmax, mode, temperature=0.0,
-                    eps=0.09, delta=0.3, bf16=False, topk_hook=None):
+                    eps=0.09, delta=0.3, bf16=False, topk_hook=None, stop_token=None, max_new=None):
     """Returns (tokens: list per sequence of appended tokens, per-step records)."""
     logits, h, cK, cV, seq = prefill(params, prompt, Lmax, bf16=bf16)
     B = seq.shape[0]
     root = root_token(logits[:, -1])
     h_sel = h[:, -1]
     toks = [[] for _ in range(B)]
+    done = np.zeros(B, dtype=bool)
     records = []
     for step in range(n_steps):
         topk, _ = medusa_heads_topk(h_sel, heads["W1"], heads["W2"], tree["K"], bf16=bf16)
@@ -38,11 +42,20 @@ def medusa_generate(params, heads, tree, prompt, n_steps, Lmax, mode, temperatur
         tree_tokens, tree_pos, cart = build_candidates(tree, root, topk, seq)
         lg, hh, Kt, Vt = forward(params, tree_tokens, tree_pos, cK, cV, seq, tree["anc"], bf16=bf16)
         best, a, sel, nr, _ = evaluate_posterior(tree, lg, tree_tokens, mode, temperature, eps, delta)
-        for b, t in enumerate(accepted_tokens(cart, best, a)):
-            toks[b].extend(int(v) for v in t)
-        cK, cV, seq = kv_compact(tree, cK, cV, Kt, Vt, best, a, seq)
+        counts = None
+        if stop_token is None and max_new is None:
+            for b, t in enumerate(accepted_tokens(cart, best, a)):
+                toks[b].extend(int(v) for v in t)
+            cK, cV, seq = kv_compact(tree, cK, cV, Kt, Vt, best, a, seq)
+        else:
+            n_out = np.array([len(t) for t in toks])
+            counts, done = appended_counts(cart, best, a, stop_token, done, n_out,
+                                           max_new if max_new is not None else 1 << 30, seq, Lmax)
+            for b in range(B):
+                toks[b].extend(int(v) for v in cart[b, int(best[b]), : int(counts[b])])
+            cK, cV, seq = kv_compact_counts(tree, cK, cV, Kt, Vt, best, counts, seq)
         h_sel = hh[np.arange(B), sel]
         root = nr
         records.append(dict(topk=topk, tree_tokens=tree_tokens, best=best, accept_len=a, sel=sel,
-                            next_root=nr))
+                            next_root=nr, counts=counts, seq_len=np.array(seq, copy=True)))
     return toks, records

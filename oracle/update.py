@@ -40,3 +40,47 @@ def accepted_tokens(cart, best, accept_len):
     """List (per sequence) of the a+1 tokens appended this step."""
     return [list(np.asarray(cart[b, int(best[b]), : int(accept_len[b]) + 1], dtype=np.int64))
             for b in range(cart.shape[0])]
+
+
+def appended_counts(cart, best, accept_len, stop_token, done, n_out, max_new, seq_len, Lmax):
+    """Per-sequence stop (reading of the page's medusa_generate loop, section 二.1,
+    which ends generation once the end-of-sequence token is among the new tokens):
+    a sequence appends its a+1 accepted tokens up to and including the first
+    stop token, and no more than its remaining output room (max_new - n_out) and
+    cache room (Lmax - seq_len); a finished sequence appends nothing.  A sequence
+    finishes when it appends the stop token or its count reaches its room.
+    Returns (counts, done')."""
+    B = cart.shape[0]
+    counts = np.zeros(B, dtype=np.int64)
+    new_done = np.array(done, dtype=bool, copy=True)
+    for b in range(B):
+        if new_done[b]:
+            continue
+        toks = [int(v) for v in cart[b, int(best[b]), : int(accept_len[b]) + 1]]
+        c, fin = len(toks), False
+        if stop_token is not None and stop_token in toks:
+            c, fin = toks.index(stop_token) + 1, True
+        room = min(int(max_new) - int(n_out[b]), int(Lmax) - int(seq_len[b]))
+        if c >= room:
+            c, fin = max(room, 0), True
+        counts[b] = c
+        new_done[b] = fin
+    return counts, new_done
+
+
+def kv_compact_counts(tree, Kc, Vc, Kt, Vt, best, counts, seq_len):
+    """kv_compact with counts[b] rows (the first counts[b] nodes of the chosen path)."""
+    Kc = np.array(Kc, copy=True)
+    Vc = np.array(Vc, copy=True)
+    seq_len = np.array(seq_len, dtype=np.int64, copy=True)
+    for b in range(Kc.shape[1]):
+        c = int(counts[b])
+        if c == 0:
+            continue
+        rows = tree["retrieve"][int(best[b]), :c]
+        s = int(seq_len[b])
+        Kc[:, b, :, s:s + c, :] = np.asarray(Kt)[:, b][:, :, rows, :]
+        Vc[:, b, :, s:s + c, :] = np.asarray(Vt)[:, b][:, :, rows, :]
+        seq_len[b] = s + c
+    return Kc, Vc, seq_len
+

@@ -61,7 +61,7 @@ class StateDesc(C.Structure):
     _fields_ = [("Kc", C.c_void_p), ("Vc", C.c_void_p), ("Lmax", C.c_int64), ("seq_len", C.c_void_p),
                 ("root", C.c_void_p), ("h_sel", C.c_void_p), ("out_tokens", C.c_void_p), ("max_new", C.c_int),
                 ("n_out", C.c_void_p), ("err", C.c_void_p), ("best", C.c_void_p), ("accept_len", C.c_void_p),
-                ("sel_node", C.c_void_p)]
+                ("sel_node", C.c_void_p), ("done", C.c_void_p), ("stop_token", C.c_int32)]
 
 
 _lib = None

@@ -95,6 +95,86 @@ __global__ void compact_finalize_kernel(const medusa_tree_host* __restrict__ t, 
   seq_len[b] = s + a + 1;
 }
 
+// Per-sequence stop: the number of this step's accepted tokens a sequence
+// appends -- up to and including the first stop token (stop >= 0), and no
+// more than its output room (max_new - n) and cache room (Lmax - s); fin is set
+// when it appends the stop token or uses up a room.  The page's generation
+// loop (section 二.1) ends once the end-of-sequence token is among the new
+// tokens; a batch keeps its shape, so a finished sequence appends nothing more.
+__device__ __forceinline__ int appended_count(const medusa_tree_host* t, const int32_t* tree_tokens, int b, int a,
+                                              int bi, int s, int n, int max_new, int64_t Lmax, int stop, bool& fin) {
+  int c = a + 1;
+  fin = false;
+  if (stop >= 0)
+    for (int i = 0; i <= a; ++i)
+      if (tree_tokens[(size_t)b * t->T + t->retrieve[bi * MEDUSA_MAX_TREE + i]] == stop) {
+        c = i + 1;
+        fin = true;
+        break;
+      }
+  const int64_t room64 = min((int64_t)max_new - n, Lmax - s);
+  const int room = (int)max<int64_t>(room64, 0);
+  if (c >= room) {
+    c = room;
+    fin = true;
+  }
+  return c;
+}
+
+__device__ __forceinline__ bool compact_bad(const medusa_tree_host* t, int a, int bi, int s, int n) {
+  return a < 0 || bi < 0 || bi >= t->P || a + 1 > t->path_len[bi] || s < 0 || n < 0;
+}
+
+template <int EB>
+__global__ void compact_kv_stop_kernel(const medusa_tree_host* __restrict__ t, int B, int Hkv, int Dh, int64_t Lmax,
+                                       char* __restrict__ Kc, char* __restrict__ Vc, const char* __restrict__ Kt,
+                                       const char* __restrict__ Vt, const int32_t* __restrict__ best,
+                                       const int32_t* __restrict__ accept_len, const int32_t* __restrict__ seq_len,
+                                       const int32_t* __restrict__ tree_tokens, const int32_t* __restrict__ n_out,
+                                       int max_new, const int32_t* __restrict__ done, int stop) {
+  const int lh = blockIdx.x;  // layer * Hkv + h
+  const int b = blockIdx.y;
+  const int layer = lh / Hkv, h = lh % Hkv;
+  if (done[b]) return;
+  const int a = accept_len[b], s = seq_len[b], bi = best[b], n = n_out[b];
+  if (compact_bad(t, a, bi, s, n)) return;
+  bool fin;
+  const int c = appended_count(t, tree_tokens, b, a, bi, s, n, max_new, Lmax, stop, fin);
+  const int T = t->T;
+  char* dst = blockIdx.z == 0 ? Kc : Vc;
+  const char* src = blockIdx.z == 0 ? Kt : Vt;
+  const size_t row_bytes = (size_t)Dh * EB;
+  const size_t slab = ((size_t)layer * B + b) * Hkv + h;
+  const size_t chunks = row_bytes / 16;
+  for (size_t e = threadIdx.x; e < (size_t)c * chunks; e += blockDim.x) {
+    const int i = (int)(e / chunks);
+    const size_t ch = e % chunks;
+    const int node = t->retrieve[bi * MEDUSA_MAX_TREE + i];
+    *((uint4*)(dst + (slab * Lmax + s + i) * row_bytes) + ch) = *((const uint4*)(src + (slab * T + node) * row_bytes) + ch);
+  }
+}
+
+__global__ void compact_stop_finalize_kernel(const medusa_tree_host* __restrict__ t, int B, int64_t Lmax,
+                                             const int32_t* __restrict__ best, const int32_t* __restrict__ accept_len,
+                                             int32_t* __restrict__ seq_len, const int32_t* __restrict__ tree_tokens,
+                                             int32_t* __restrict__ out_tokens, int max_new, int32_t* __restrict__ n_out,
+                                             int32_t* __restrict__ done, int stop, int32_t* __restrict__ err_flag) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B || done[b]) return;
+  const int a = accept_len[b], s = seq_len[b], bi = best[b], n = n_out[b];
+  if (compact_bad(t, a, bi, s, n)) {
+    if (err_flag) *err_flag = 1;
+    return;
+  }
+  bool fin;
+  const int c = appended_count(t, tree_tokens, b, a, bi, s, n, max_new, Lmax, stop, fin);
+  for (int i = 0; i < c; ++i)
+    out_tokens[(size_t)b * max_new + n + i] = tree_tokens[(size_t)b * t->T + t->retrieve[bi * MEDUSA_MAX_TREE + i]];
+  n_out[b] = n + c;
+  seq_len[b] = s + c;
+  if (fin) done[b] = 1;
+}
+
 }  // namespace
 
 extern "C" int tree_build_candidates(const medusa_tree* t, int B, int H, int K, const int32_t* root,
@@ -144,3 +224,39 @@ extern "C" int kv_compact(int dtype, const medusa_tree* t, int n_layers, int B, 
                      accept_len, seq_len, tree_tokens, out_tokens, max_new, n_out, err_flag);
   return check_launch("kv_compact finalize");
 }
+
+namespace medusa {
+
+int kv_compact_stop(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax, void* Kc,
+                    void* Vc, const void* Kt, const void* Vt, const int32_t* best, const int32_t* accept_len,
+                    int32_t* seq_len, const int32_t* tree_tokens, int32_t* out_tokens, int max_new, int32_t* n_out,
+                    int32_t* done, int stop_token, int32_t* err_flag, hipStream_t stream) {
+  MEDUSA_REQUIRE(t && dtype_ok(dtype), MEDUSA_ERR_ARG, "kv_compact_stop: bad tree or dtype");
+  MEDUSA_REQUIRE(n_layers >= 0 && B >= 0 && Hkv > 0 && Dh > 0 && Lmax > 0, MEDUSA_ERR_ARG,
+                 "kv_compact_stop: bad sizes");
+  MEDUSA_REQUIRE(((size_t)Dh * dtype_size(dtype)) % 16 == 0, MEDUSA_ERR_UNSUPPORTED,
+                 "kv_compact_stop: a K/V row must be a multiple of 16 bytes");
+  if (B == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(best && accept_len && seq_len && tree_tokens && out_tokens && n_out && done && max_new > 0,
+                 MEDUSA_ERR_ARG, "kv_compact_stop: null pointer");
+  if (n_layers > 0) {
+    MEDUSA_REQUIRE(Kc && Vc && Kt && Vt, MEDUSA_ERR_ARG, "kv_compact_stop: null K/V pointer");
+    dim3 grid(n_layers * Hkv, B, 2);
+    if (dtype == MEDUSA_BF16)
+      hipLaunchKernelGGL(compact_kv_stop_kernel<2>, grid, dim3(128), 0, stream, t->dev, B, Hkv, Dh, Lmax, (char*)Kc,
+                         (char*)Vc, (const char*)Kt, (const char*)Vt, best, accept_len, seq_len, tree_tokens, n_out,
+                         max_new, done, stop_token);
+    else
+      hipLaunchKernelGGL(compact_kv_stop_kernel<4>, grid, dim3(128), 0, stream, t->dev, B, Hkv, Dh, Lmax, (char*)Kc,
+                         (char*)Vc, (const char*)Kt, (const char*)Vt, best, accept_len, seq_len, tree_tokens, n_out,
+                         max_new, done, stop_token);
+    int rc = check_launch("kv_compact_stop");
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(compact_stop_finalize_kernel, dim3((B + 63) / 64), dim3(64), 0, stream, t->dev, B, Lmax, best,
+                     accept_len, seq_len, tree_tokens, out_tokens, max_new, n_out, done, stop_token, err_flag);
+  return check_launch("kv_compact_stop finalize");
+}
+
+}  // namespace medusa
+

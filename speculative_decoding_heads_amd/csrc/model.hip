@@ -240,6 +240,7 @@ extern "C" int medusa_prefill(const medusa_model* m, int B, int S, const int32_t
   hipLaunchKernelGGL(fill_i32_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, st->seq_len, B, 0);
   if (st->n_out) hipLaunchKernelGGL(fill_i32_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, st->n_out, B, 0);
   if (st->err) hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, stream, st->err, 1, 0);
+  if (st->done) hipLaunchKernelGGL(fill_i32_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, st->done, B, 0);
   CK(check_launch("prefill init"));
   for (int c0 = 0; c0 < S; c0 += MEDUSA_MAX_TREE) {
     const int Sc = (S - c0) < MEDUSA_MAX_TREE ? (S - c0) : MEDUSA_MAX_TREE;
@@ -307,6 +308,21 @@ size_t step_layout(const medusa_model* m, const medusa_tree* t, int B, int64_t L
 }
 }  // namespace
 
+namespace {
+// KV compaction and token append of a step, with per-sequence stop when the
+// state carries done flags
+int compact_state(const medusa_model* m, const medusa_tree* t, int B, medusa_state* st, const void* Kt,
+                  const void* Vt, const int32_t* tok, hipStream_t stream) {
+  if (st->done)
+    return kv_compact_stop(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, Kt, Vt,
+                           st->best, st->accept_len, st->seq_len, tok, st->out_tokens, st->max_new, st->n_out,
+                           st->done, st->stop_token, st->err, stream);
+  return kv_compact(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, Kt, Vt,
+                    st->best, st->accept_len, st->seq_len, tok, st->out_tokens, st->max_new, st->n_out, st->err,
+                    stream);
+}
+}  // namespace
+
 extern "C" size_t medusa_step_workspace_size(const medusa_model* m, const medusa_tree* t, int B, int64_t L_hint) {
   if (!m || !t || B <= 0 || m->n_medusa <= 0) return 0;
   return step_layout(m, t, B, L_hint, nullptr, nullptr);
@@ -338,8 +354,7 @@ extern "C" int medusa_step(const medusa_model* m, const medusa_tree* t, int B, i
                     s.logits, s.h, s.fws, s.fws_bytes, stream));
   CK(evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best, st->accept_len,
                         st->sel_node, st->root, s.pws, s.pws_bytes, stream));
-  CK(kv_compact(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, s.Kt, s.Vt,
-                st->best, st->accept_len, st->seq_len, s.tok, st->out_tokens, st->max_new, st->n_out, st->err, stream));
+  CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, stream));
   CK(medusa_gather_rows(m->dtype, B, T, m->d, s.h, st->sel_node, st->h_sel, stream));
   return MEDUSA_OK;
 #undef CK
@@ -420,8 +435,7 @@ extern "C" int medusa_step_fused(const medusa_model* m, const medusa_tree* t, in
                        f.hws, f.hws_bytes, stream));
   CK(evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best, st->accept_len,
                         st->sel_node, st->root, s.pws, s.pws_bytes, stream));
-  CK(kv_compact(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, s.Kt, s.Vt,
-                st->best, st->accept_len, st->seq_len, s.tok, st->out_tokens, st->max_new, st->n_out, st->err, stream));
+  CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, stream));
   CK(medusa_gather_rows(m->dtype, B, T, m->d, s.h, st->sel_node, st->h_sel, stream));
   hipLaunchKernelGGL(gather_topk_kernel, dim3(B), dim3(64), 0, stream, T, H * K, f.topk_all, st->sel_node,
                      topk_carry);

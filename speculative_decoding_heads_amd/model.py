@@ -97,7 +97,9 @@ class Model:
 class State:
     """Device buffers of B sequences in generation (medusa_state)."""
 
-    def __init__(self, model, B, Lmax, max_new):
+    def __init__(self, model, B, Lmax, max_new, stop_token=None):
+        """stop_token: per-sequence stop (an int >= 0, or -1 for output/cache room only);
+        None keeps the plain behaviour (every step appends all accepted tokens)."""
         torch = _torch()
         dev = model.device
         i32 = lambda *s: torch.zeros(s, dtype=torch.int32, device=dev)
@@ -109,9 +111,11 @@ class State:
         self.out_tokens = i32(B, max(max_new, 1))
         self.err = i32(1)
         self.best, self.accept_len, self.sel_node = i32(B), i32(B), i32(B)
+        self.done = i32(B) if stop_token is not None else None
+        self.stop_token = -1 if stop_token is None else int(stop_token)
         self.desc = L.StateDesc(ptr(self.Kc), ptr(self.Vc), Lmax, ptr(self.seq_len), ptr(self.root), ptr(self.h_sel),
                                 ptr(self.out_tokens), max_new, ptr(self.n_out), ptr(self.err), ptr(self.best),
-                                ptr(self.accept_len), ptr(self.sel_node))
+                                ptr(self.accept_len), ptr(self.sel_node), ptr(self.done), self.stop_token)
 
 
 def prefill(model, state, prompt, ws=None):

@@ -107,6 +107,56 @@ def test_tiny_fp32_fused_draft_verify(dev):
         assert [int(a[b]) for a in acc] == [int(r["accept_len"][b]) for r in orecs]
 
 
+@pytest.mark.parametrize("use_stop", [True, False])
+def test_tiny_fp32_per_sequence_stop(dev, use_stop):
+    """Per-sequence stop on the GPU equals the oracle loop token for token: a stop
+    token inside a step's three accepted tokens ends sequence 0 there, the other
+    sequence runs on to its output room (30 tokens); without a stop token the
+    output room alone ends both.  Identical candidate lists on both sides (two
+    forced plain-greedy continuations, the rest fixed tokens)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd.model import Model, State, prefill, step
+    say("e2e tiny fp32 per-sequence stop", use_stop)
+    params, heads = tiny_model(0)
+    prompt = prompt_tokens(100, 2, TinyConfig.prompt_len, TinyConfig.vocab)
+    plain = greedy_decode(params, prompt, 60, 256)
+    k = next(i for i in range(4, 40) if i % 3 != 2 and int(plain[0, i]) not in plain[0, :i].tolist()
+             and int(plain[0, i]) not in plain[1, :30].tolist())
+    stop = int(plain[0, k]) if use_stop else -1
+
+    def cands(produced_lens):
+        ov = np.zeros((2, 2, 3), np.int64)
+        for b in range(2):
+            n = int(produced_lens[b])
+            ov[b] = np.arange(6).reshape(2, 3) + 7
+            ov[b, 0, 0] = plain[b, n + 1]
+            ov[b, 1, 0] = plain[b, n + 2]
+        return ov
+
+    n_steps = 14
+    omed, orecs = medusa_generate(params, heads, tree_buffers(TWO_HEAD_CHOICES), prompt, n_steps, 256, GREEDY,
+                                  topk_hook=lambda s, tk, prod: cands([len(p) for p in prod]),
+                                  stop_token=stop if use_stop else None, max_new=30)
+    P, H = _upload(params, heads, torch.float32, dev)
+    model = Model(P, H, max_pos=1024)
+    tree = api.Tree(TWO_HEAD_CHOICES)
+    st = State(model, 2, 256, 30, stop_token=stop)
+    prefill(model, st, torch.from_numpy(prompt.astype(np.int32)).to(dev))
+    for _ in range(n_steps):
+        ov = torch.from_numpy(cands(to_np(st.n_out)).astype(np.int32)).to(dev)
+        step(model, tree, st, GREEDY, L_hint=256, topk_override=ov)
+    torch.cuda.synchronize()
+    assert int(to_np(st.err)[0]) == 0
+    n, toks = to_np(st.n_out), to_np(st.out_tokens)
+    for b in range(2):
+        assert toks[b, : n[b]].tolist() == omed[b]
+    assert to_np(st.seq_len).tolist() == [int(x) for x in orecs[-1]["seq_len"]]
+    assert to_np(st.done).tolist() == [1, 1]
+    if use_stop:
+        assert omed[0] == plain[0, : k + 1].tolist()
+
+
 @pytest.mark.parametrize("ranks", [(0, 0), (1, 2), (1, None)])
 def test_tiny_fp32_forced_acceptance(dev, ranks):
     say("e2e tiny fp32 forced acceptance", ranks)

@@ -120,6 +120,54 @@ def test_forced_acceptance_keeps_greedy_output(ranks):
     assert all(int(r["accept_len"][0]) >= want for r in recs)
 
 
+def _forced_two(plain):
+    """Hook that makes every step accept two candidates (three tokens) per sequence."""
+    def hook(step, topk, produced):
+        topk = topk.copy()
+        for b, prod in enumerate(produced):
+            n = len(prod)
+            topk[b, 0, 0] = plain[b, n + 1]
+            topk[b, 1, 0] = plain[b, n + 2]
+        return topk
+    return hook
+
+
+def test_stop_token_truncates_plain_greedy():
+    """Per-sequence stop: the output is plain greedy decoding up to and including the
+    first stop token (here one that falls inside a step's three accepted tokens),
+    after which the sequence appends nothing and its length stays; the other
+    sequence of the batch runs on to its output room."""
+    params, heads = tiny_model(0)
+    t = tree_buffers(TWO_HEAD_CHOICES)
+    prompt = prompt_tokens(100, 2, TinyConfig.prompt_len, TinyConfig.vocab)
+    plain = greedy_decode(params, prompt, 60, 160)
+    k = next(i for i in range(4, 40) if i % 3 != 2 and int(plain[0, i]) not in plain[0, :i].tolist()
+             and int(plain[0, i]) not in plain[1, :30].tolist())
+    stop = int(plain[0, k])
+    out, recs = medusa_generate(params, heads, t, prompt, 14, 160, GREEDY, topk_hook=_forced_two(plain),
+                                stop_token=stop, max_new=30)
+    assert out[0] == plain[0, :k + 1].tolist()
+    assert out[1] == plain[1, :30].tolist()
+    P = TinyConfig.prompt_len
+    assert [int(r["seq_len"][0]) for r in recs][-1] == P + k + 1
+    s_after = [int(r["seq_len"][0]) for r in recs if int(r["seq_len"][0]) == P + k + 1]
+    assert len(s_after) >= 2  # the stopped sequence keeps its length over later steps
+
+
+def test_output_room_caps_without_stop_token():
+    """No stop token, max_new = 7 with three tokens accepted per step: the third
+    step appends one token, and the output is the first 7 plain-greedy tokens."""
+    params, heads = tiny_model(0)
+    t = tree_buffers(TWO_HEAD_CHOICES)
+    prompt = prompt_tokens(100, 2, TinyConfig.prompt_len, TinyConfig.vocab)
+    plain = greedy_decode(params, prompt, 40, 160)
+    out, recs = medusa_generate(params, heads, t, prompt, 5, 160, GREEDY, topk_hook=_forced_two(plain),
+                                max_new=7)
+    for b in range(2):
+        assert out[b] == plain[b, :7].tolist()
+    assert [int(r["counts"][0]) for r in recs] == [3, 3, 1, 0, 0]
+
+
 def test_bf16_rounding_matches_torch():
     import torch
     from oracle.numerics import round_bf16
