@@ -26,7 +26,7 @@ struct NodeStat {
   float m, Z, thr;
 };
 
-constexpr int kStatThreads = 512;
+constexpr int kStatThreads = 1024;
 
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) {
@@ -46,17 +46,19 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
   __shared__ float s_f[kStatThreads / 64];
   const int lane = tid & 63, w = tid >> 6;
 
-  // pass 1: argmax, and for typical an online sum of exp((x - running max)/tau)
+  // pass 1: argmax, and for typical an online sum of exp((x - running max)/tau),
+  // as 2^((x - max) * log2(e)/tau) on the hardware base-2 exponential
+  const float c2 = inv_tau * 1.4426950408889634f;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   float z = 0.f;
   auto visit = [&](float v, int k) {
     if (v > bv) {  // strictly greater keeps the lowest index of this thread's stripe
-      if (typical) z = z * expf((bv - v) * inv_tau) + 1.0f;
+      if (typical) z = z * __builtin_amdgcn_exp2f((bv - v) * c2) + 1.0f;
       bv = v;
       bi = k;
     } else if (typical) {
-      z += expf((v - bv) * inv_tau);
+      z += __builtin_amdgcn_exp2f((v - bv) * c2);
     }
   };
   const bool vec = (V % 4) == 0;
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
   }
   auto merge = [&](float v2, int i2, float z2) {
     const float m = fmaxf(bv, v2);
-    if (typical && m != -INFINITY) z = z * expf((bv - m) * inv_tau) + z2 * expf((v2 - m) * inv_tau);
+    if (typical && m != -INFINITY)
+      z = z * __builtin_amdgcn_exp2f((bv - m) * c2) + z2 * __builtin_amdgcn_exp2f((v2 - m) * c2);
     argmax_merge(bv, bi, v2, i2);
   };
 #pragma unroll
@@ -102,11 +105,12 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
   const float m = bv;
   const float Z = z;
   const float invZ = 1.0f / Z;
-  // pass 2: H = -sum q log(q + 1e-5)
+  // pass 2: H = -sum q log(q + 1e-5), natural log as log2 * ln 2 (the ln 2 is
+  // applied once to the sum)
   float hsum = 0.f;
   auto hterm = [&](float v) {
-    const float q = expf((v - m) * inv_tau) * invZ;
-    hsum += q * logf(q + 1e-5f);
+    const float q = __builtin_amdgcn_exp2f((v - m) * c2) * invZ;
+    hsum += q * __builtin_amdgcn_logf(q + 1e-5f);
   };
   if (vec) {
     const float4* x4 = (const float4*)x;
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
   if (tid == 0) {
     float hs = 0.f;
     for (int j = 0; j < kStatThreads / 64; ++j) hs += s_f[j];
-    const float H = -hs;
+    const float H = -hs * 0.6931471805599453f;
     const float thr = fminf(eps, delta * expf(-H));
     out[(size_t)b * T + u] = NodeStat{bi, m, Z, thr};
   }
