@@ -123,6 +123,18 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
   const int kvh = blockIdx.y, b = blockIdx.z;
   const size_t slab = (size_t)b * Hkv + kvh;
   const size_t base = slab * n_splits * (size_t)R + rr;  // partial row of split s: base + s * R
+  const int d0 = lane * 4 < Dh ? lane * 4 : 0;  // lanes past Dh load a valid column and store nothing
+  // The first CB splits' partial rows do not depend on the weights: their
+  // loads go out with the maximum/sum loads, so n_splits <= CB costs one
+  // memory round trip (a split index past n_splits re-reads the last split
+  // and is left out of the sum).
+  constexpr int CB = 8;
+  float4 v[CB];
+#pragma unroll
+  for (int u = 0; u < CB; ++u) {
+    const int su = u < n_splits ? u : n_splits - 1;
+    v[u] = *(const float4*)(ws_o + (base + (size_t)su * R) * Dh + d0);
+  }
   float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
   if (lane < n_splits) {
     m0 = ws_ml[(base + (size_t)lane * R) * 2];
@@ -141,32 +153,34 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
 #pragma unroll
   for (int o = 16; o >= 1; o >>= 1) lt += __shfl_xor(lt, o, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  const int d0 = lane * 4 < Dh ? lane * 4 : 0;  // lanes past Dh load a valid column and store nothing
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 4 <= n_splits; s += 4) {
-    float4 v[4];
-    float w[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v[u] = *(const float4*)(ws_o + (base + (size_t)(s + u) * R) * Dh + d0);
-      w[u] = __shfl(s + u < 32 ? w0 : w1, (s + u) & 31, 32);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[0] += v[u].x * w[u];
-      acc[1] += v[u].y * w[u];
-      acc[2] += v[u].z * w[u];
-      acc[3] += v[u].w * w[u];
+  for (int u = 0; u < CB; ++u) {
+    const float w = __shfl(w0, u, 32);  // split u < 32: its weight sits in lane u's w0
+    if (u < n_splits) {
+      acc[0] += v[u].x * w;
+      acc[1] += v[u].y * w;
+      acc[2] += v[u].z * w;
+      acc[3] += v[u].w * w;
     }
   }
-  for (; s < n_splits; ++s) {
-    const float4 v = *(const float4*)(ws_o + (base + (size_t)s * R) * Dh + d0);
-    const float w = __shfl(s < 32 ? w0 : w1, s & 31, 32);
-    acc[0] += v.x * w;
-    acc[1] += v.y * w;
-    acc[2] += v.z * w;
-    acc[3] += v.w * w;
+  for (int s0 = CB; s0 < n_splits; s0 += CB) {
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int su = s0 + u < n_splits ? s0 + u : n_splits - 1;
+      v[u] = *(const float4*)(ws_o + (base + (size_t)su * R) * Dh + d0);
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int s = s0 + u;
+      const float w = __shfl(s < 32 ? w0 : w1, s & 31, 32);
+      if (s < n_splits) {
+        acc[0] += v[u].x * w;
+        acc[1] += v[u].y * w;
+        acc[2] += v[u].z * w;
+        acc[3] += v[u].w * w;
+      }
+    }
   }
   if (!valid || lane * 4 >= Dh) return;
   const int node = r / G, g = r % G;

@@ -965,9 +965,12 @@ namespace {
 // SK > 0: acc = sum_s part[s][m][:] in split order, x[m,:] = bf16(x[m,:] + acc)
 // is stored; SK == 0: x is only read.  Then y[m,:] = bf16(x[m,:] * inv * g)
 // with inv = 1 / sqrt(mean(x[m,:]^2) + eps) taken over the stored bf16 x.
-// Every global read of a row (x, the partials, g) is issued before the first
-// use, so a row costs one memory round trip plus the block reduction.
+// The reads of x and g and of the partials are issued before their first use,
+// the partials RN_SKB splits at a time, so a row costs ceil(SK / RN_SKB)
+// memory round trips plus the block reduction (a loop that waited for each
+// split's load before the next measured one round trip per split).
 constexpr int RN_THREADS = 512;
+constexpr int RN_SKB = 4;
 template <int NV>
 __global__ __launch_bounds__(RN_THREADS) void resid_rmsnorm_kernel(int M, int N, int SK,
                                                                    const float* __restrict__ part,
@@ -993,11 +996,27 @@ __global__ __launch_bounds__(RN_THREADS) void resid_rmsnorm_kernel(int M, int N,
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[q][i] = 0.f;
     if (n >= N) continue;
-    for (int sp = 0; sp < SK; ++sp) {
-      const float4* pp = (const float4*)(part + ((size_t)sp * M + m) * N + n);
-      const float4 a = pp[0], b = pp[1];
-      v[q][0] += a.x; v[q][1] += a.y; v[q][2] += a.z; v[q][3] += a.w;
-      v[q][4] += b.x; v[q][5] += b.y; v[q][6] += b.z; v[q][7] += b.w;
+    // RN_SKB splits per batch, all loads of a batch in flight together (a
+    // tail batch re-reads the last split and leaves the copies out of the sum)
+    for (int s0 = 0; s0 < SK; s0 += RN_SKB) {
+      float4 a[RN_SKB], b[RN_SKB];
+#pragma unroll
+      for (int u = 0; u < RN_SKB; ++u) {
+        const int sp = s0 + u < SK ? s0 + u : SK - 1;
+        const float4* pp = (const float4*)(part + ((size_t)sp * M + m) * N + n);
+        a[u] = pp[0];
+        b[u] = pp[1];
+      }
+      // a select, not a branch, so that the loads stay ahead of every use
+      // (adding +0 leaves a sum that started at +0 unchanged)
+#pragma unroll
+      for (int u = 0; u < RN_SKB; ++u) {
+        const bool t = s0 + u < SK;
+        v[q][0] += t ? a[u].x : 0.f; v[q][1] += t ? a[u].y : 0.f;
+        v[q][2] += t ? a[u].z : 0.f; v[q][3] += t ? a[u].w : 0.f;
+        v[q][4] += t ? b[u].x : 0.f; v[q][5] += t ? b[u].y : 0.f;
+        v[q][6] += t ? b[u].z : 0.f; v[q][7] += t ? b[u].w : 0.f;
+      }
     }
   }
   float ss = 0.f;

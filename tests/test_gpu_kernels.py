@@ -296,6 +296,8 @@ def test_gemm_swiglu_96_row_tiles(dev):
 
 @pytest.mark.parametrize("dtype_name,M,N,K", [("bf16", 64, 4096, 4096), ("bf16", 64, 4096, 11008),
                                               ("bf16", 5, 512, 256), ("bf16", 40, 1000, 1056),
+                                              # K splits of 3 and 5: partial batches of the split loads
+                                              ("bf16", 64, 1024, 768), ("bf16", 64, 1024, 1280),
                                               ("fp32", 5, 512, 256)])
 def test_gemm_resid_rmsnorm(dev, dtype_name, M, N, K):
     import torch
