@@ -223,25 +223,27 @@ def _small_bf16_model(seed, heads_kv_dim=(8, 4, 64)):
 
 
 # GQA with head size 64 and MHA with head size 128: both take the fused
-# projection + rotary epilogue (64 tree rows x batch 2 = 128 product rows)
-@pytest.mark.parametrize("heads_kv_dim", [(8, 4, 64), (4, 4, 128)])
-def test_bf16_forward_vs_oracle(dev, heads_kv_dim):
+# projection + rotary epilogue (64 tree rows x batch 2 = 128 product rows);
+# at batch 1 (64 rows, one activation tile) MHA with head sizes 128 and 64
+# takes the 48-row q/K/V workgroups
+@pytest.mark.parametrize("heads_kv_dim,B", [((8, 4, 64), 2), ((4, 4, 128), 2), ((4, 4, 128), 1), ((8, 8, 64), 1)])
+def test_bf16_forward_vs_oracle(dev, heads_kv_dim, B):
     import torch
     from speculative_decoding_heads_amd import api
     from speculative_decoding_heads_amd.model import Model
-    say("e2e bf16 forward vs oracle", heads_kv_dim)
+    say("e2e bf16 forward vs oracle", heads_kv_dim, "batch", B)
     (params, heads), Cfg = _small_bf16_model(3, heads_kv_dim)
     P, H = _upload(params, heads, torch.bfloat16, dev)
     model = Model(P, H, max_pos=1024)
     tree = api.Tree(PAGE_TREE_CHOICES)
     ot = tree_buffers(PAGE_TREE_CHOICES)
     rng = np.random.default_rng(4)
-    B, L, Lmax = 2, 150, 192
+    L, Lmax = 150, 192
     NL, Hkv, Dh = Cfg.n_layers, Cfg.n_kv_heads, Cfg.head_dim
     from workloads import bf16_round
     Kc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
     Vc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
-    seq = np.array([L, L - 37], np.int32)
+    seq = np.array([L, L - 37][:B], np.int32)
     toks = rng.integers(0, Cfg.vocab, (B, 64)).astype(np.int32)
     pos = (seq[:, None] + ot["depth"][None, :]).astype(np.int32)
     d = lambda x: torch.from_numpy(x).to(dev)
