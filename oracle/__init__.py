@@ -24,6 +24,8 @@ decoder     pre-norm decoder forward over a batch of new tokens, plain greedy de
 posterior   greedy and typical ("fast") acceptance with longest-path choice
 update      KV compaction / token append after acceptance
 loop        whole Medusa generation loop and the plain greedy baseline
+calib       tree calibration: expected accepted length, the best tree of n
+            nodes from per-(depth, rank) acceptance, teacher-forced head hits
 
 Every function that has no independent pin says "parity unpinned" in its
 docstring; all others are pinned by ``tests/test_oracle_*.py``.
