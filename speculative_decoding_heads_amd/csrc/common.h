@@ -79,8 +79,8 @@ int resid_rmsnorm_bf16(int M, int N, int SK, const float* part, bf16_t* x, const
 
 // Fused q/K/V projection + rotary embedding for the bf16 verify forward
 // (gemm.hip); MEDUSA_ERR_UNSUPPORTED without launching for shapes it does not
-// take (M <= 32, Dh % 64 != 0), in which case the caller runs medusa_gemm +
-// medusa_rope_split.
+// take (Dh % 64 != 0, or M <= 32 under MEDUSA_GEMM_DMA_MIN_M = 33), in which
+// case the caller runs medusa_gemm + medusa_rope_split.
 int gemm_qkv_rope_bf16(int B, int T, int K, int Hq, int Hkv, int Dh, const bf16_t* A, const bf16_t* W,
                        const int32_t* pos, const float* cos_t, const float* sin_t, int max_pos, bf16_t* q_out,
                        bf16_t* k_out, bf16_t* v_out, hipStream_t stream);

@@ -7,7 +7,12 @@
 // Both are weight-streaming products with few rows (M = batch or batch*T), so
 // the bf16 kernel is built for HBM streaming, not for square tiles:
 //
-//  * bf16: a wave owns 32 (M > 32) or 64 rows of W and up to 64 rows of A; W is
+//  * bf16, every M (one 64-row activation tile per workgroup, rows past M
+//    re-reading row M - 1): gemm_dma_kernel when K % 64 == 0 (both operands
+//    into an LDS ring by direct loads), gemm_lds_kernel otherwise (weights
+//    through registers, activation in LDS); both below.
+//  * bf16 register kernel (gemm_bf16_kernel; taken only under the tuning
+//    variables for M <= 32): a wave owns 32 or 64 rows of W and up to 64 rows of A; W is
 //    the MFMA A-operand (16x16x32 bf16, fp32 accumulate) so each lane loads 16
 //    contiguous bytes of one W row per k-step.  The four waves of a workgroup
 //    take neighbouring W rows over the same k range (their A loads coincide and
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(GTHR) void gemm_bf16_kernel(int M, int N, int K, co
   store_tile<NR, MB>(acc, n0, m0, M, N, SK, ks, bz, e, sC, sR, A, part, l16, lg);
 }
 
-// Kernel for M > 32.  The NWV waves of a workgroup (4, or 3 when 96-row
+// 64-row activation tile kernel (K % 64 != 0).  The NWV waves of a workgroup (4, or 3 when 96-row
 // workgroup tiles spread a product more evenly over the CUs) own neighbouring
 // (NR*16)-row W tiles and walk the same k range; the workgroup stages the 64 A
 // rows of each chunk (U k-steps) once in LDS, so A costs one global read per
@@ -558,7 +563,7 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t off, uint32_t 
                : "memory", "m0");
 }
 
-// Streaming kernel for M > 32 with a deep ring of LDS chunk buffers.  Same
+// Streaming kernel for every M (K % 64 == 0) with a deep ring of LDS chunk buffers.  Same
 // tile ownership and accumulator layout as gemm_lds_kernel (NWV waves, each
 // NR*16 W rows, 64 A rows, 16x16x32 products), but both operands travel
 // global -> LDS by 16-byte direct loads, so the depth of the pipeline is set
@@ -736,8 +741,8 @@ struct GemmPlan {
   int SK, MB, NR, U, m_tiles, n_tiles;
   int NWV;   // gemm_lds_kernel: waves per workgroup (4, or 3 for 96-row tiles)
   bool KW;   // register kernel: the four waves split K
-  bool LDS;  // M > 32: A staged in LDS (gemm_lds_kernel)
-  bool DMA;  // M > 32: both operands by direct loads into an LDS ring (gemm_dma_kernel)
+  bool LDS;  // 64-row activation tile: A staged in LDS (gemm_lds_kernel)
+  bool DMA;  // ... both operands by direct loads into an LDS ring (gemm_dma_kernel)
   size_t part_bytes;
 };
 
@@ -748,19 +753,30 @@ int env_int(const char* name, int dflt) {
 
 // Tile shape, pipeline depth and K split for one product.  The MEDUSA_GEMM_*
 // environment variables override the defaults for tuning runs only.
+// Smallest M that takes the 64-row activation tile (gemm_lds_kernel /
+// gemm_dma_kernel; rows past M re-read row M - 1): every M by default -- the
+// direct-load kernel streams the weights faster than the register kernels
+// even at M = 1 (Medusa heads at batch 1) -- or MEDUSA_GEMM_DMA_MIN_M (1..33,
+// tuning runs; 33 sends M <= 32 to gemm_bf16_kernel).
+int tile64_min_m() {
+  static const int v = env_int("MEDUSA_GEMM_DMA_MIN_M", 1);
+  return v < 1 ? 1 : (v > 33 ? 33 : v);
+}
+
 GemmPlan gemm_plan(int M, int N, int K, int batch) {
   static const int e_nr4 = env_int("MEDUSA_GEMM_NR4", 0);   // register kernel: 64 W rows per wave at M > 32
   static const int e_kw = env_int("MEDUSA_GEMM_KW", 1);     // register kernel: waves split K
-  static const int e_lds = env_int("MEDUSA_GEMM_LDS", 1);   // M > 32 on gemm_lds_kernel
+  static const int e_lds = env_int("MEDUSA_GEMM_LDS", 1);   // 0: the register kernel for every M
   static const int e_lnr = env_int("MEDUSA_GEMM_LNR", 0);   // gemm_lds_kernel: W row blocks per wave (1 | 2)
   static const int e_u = env_int("MEDUSA_GEMM_U", 2);       // k-steps per chunk cap (1 | 2 | 4)
   static const int e_waves = env_int("MEDUSA_GEMM_WAVES", 1024);
   static const int e_sk = env_int("MEDUSA_GEMM_SK", 0);     // forced K split (0: from the wave target)
-  static const int e_dma = env_int("MEDUSA_GEMM_DMA", 1);   // M > 32 on gemm_dma_kernel when the shape allows
+  static const int e_dma = env_int("MEDUSA_GEMM_DMA", 1);   // 64-row tiles on gemm_dma_kernel when the shape allows
   GemmPlan p;
   p.DMA = false;
   const int mrows = M < GM ? M : GM;
   p.MB = mrows <= 16 ? 1 : (mrows <= 32 ? 2 : 4);
+  if (M >= tile64_min_m()) p.MB = 4;
   p.m_tiles = (M + GM - 1) / GM;
   p.LDS = p.MB == 4 && e_lds;
   p.KW = e_kw && !p.LDS;
@@ -1083,7 +1099,7 @@ int resid_rmsnorm_bf16(int M, int N, int SK, const float* part, bf16_t* x, const
 
 namespace medusa {
 
-// Fused q/K/V projection with rotary embedding (bf16, M > 32, Dh % 64 == 0):
+// Fused q/K/V projection with rotary embedding (bf16, M >= tile64_min_m(), Dh % 64 == 0):
 // qkv = A W^T for W = [Hq q heads; Hkv k heads; Hkv v heads] x Dh rows, then
 // q [B, T, Hq, Dh] and Kt [B, Hkv, T, Dh] rotated at pos[b*T + t], Vt as is.
 // Returns MEDUSA_ERR_UNSUPPORTED (nothing launched) for shapes it does not take.
@@ -1091,7 +1107,7 @@ int gemm_qkv_rope_bf16(int B, int T, int K, int Hq, int Hkv, int Dh, const bf16_
                        const int32_t* pos, const float* cos_t, const float* sin_t, int max_pos, bf16_t* q_out,
                        bf16_t* k_out, bf16_t* v_out, hipStream_t stream) {
   const int M = B * T, N = (Hq + 2 * Hkv) * Dh;
-  if (M <= 32 || Dh % 64 || K % GK || K % 8) return MEDUSA_ERR_UNSUPPORTED;
+  if (M < tile64_min_m() || Dh % 64 || K % GK || K % 8) return MEDUSA_ERR_UNSUPPORTED;
   GemmPlan p = gemm_plan(M, N, K, 1);
   if (!p.LDS) return MEDUSA_ERR_UNSUPPORTED;
   p.NR = 1;
