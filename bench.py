@@ -20,6 +20,10 @@ Also measured (same JSON line):
                  at batch 1, prefix 1024, against 8 TB/s
   prefix_sweep   the same step (eager launches) at prefixes 4k, 16k and 64k, the cache
                  filled with N(0,1) keys and values (5 timed steps each)
+  tree_size_sweep
+                 the step with trees of 8..64 nodes that medusa_tree_from_acceptance
+                 builds from a synthetic per-(depth, rank) acceptance table: step time,
+                 the table's expected tokens per step and their ratio
   heads_all_tree_nodes
                  medusa_heads_topk on the hidden states of every node of 8 sequences'
                  64-node trees (512 rows: the heads applied inside the verify forward),
@@ -167,7 +171,8 @@ def main():
     from speculative_decoding_heads_amd._lib import EPI_F32, EPI_RESID, EPI_SWIGLU, TYPICAL, lib
     from speculative_decoding_heads_amd.model import (Model, State, StepGraph, init_topk_carry, prefill, step,
                                                       step_fused, step_fused_workspace_size, step_workspace_size)
-    from workloads import SevenBConfig, model_weights_torch, prompt_tokens, seeded_tree_choices, torch_normal
+    from workloads import (SevenBConfig, acceptance_table, model_weights_torch, prompt_tokens, seeded_tree_choices,
+                           torch_normal)
 
     dev = torch.device("cuda:0")
     cfg = SevenBConfig
@@ -322,6 +327,35 @@ def main():
         del st2, ws2
         torch.cuda.empty_cache()
 
+    # ---- tree size: trees of n nodes built by the library (medusa_tree_from_acceptance)
+    # from a synthetic per-(depth, rank) acceptance table; the step time at each size,
+    # the table's expected tokens per step, and their ratio (speed vs candidate count)
+    calib_acc = acceptance_table(cfg.n_medusa, 10)
+    tree_sweep = {}
+    for n_nodes in (8, 16, 24, 32, 48, 64):
+        t_choices, e_acc = api.tree_from_acceptance(calib_acc, n_nodes)
+        tr = api.Tree(t_choices, K=10)
+        ws3 = torch.empty(step_workspace_size(model, tr, B, Lmax), dtype=torch.uint8, device=dev)
+
+        def tree_step():
+            st.seq_len.copy_(base_seq)
+            st.n_out.zero_()
+            step(model, tr, st, TYPICAL, tau, eps, delta, L_hint=Lmax, ws=ws3)
+
+        for _ in range(2):
+            tree_step()
+        torch.cuda.synchronize()
+        nrep = 5
+        with Timer() as tt:
+            for _ in range(nrep):
+                tree_step()
+        ms = tt.ms() / nrep
+        tree_sweep[str(n_nodes)] = {"ms_per_step": round(ms, 4), "expected_tokens_per_step": round(1.0 + e_acc, 4),
+                                    "projected_tok_per_s": round((1.0 + e_acc) * 1e3 / ms, 2)}
+        log("tree of %d nodes: %.3f ms/step, expected %.3f tokens/step" % (n_nodes, ms, 1.0 + e_acc))
+        del tr, ws3
+    assert int(st.err[0]) == 0, "state error flag set"
+
     # ---- dominant kernel: the gate/up projection at M = 64 rows, over the 32 layers' weights
     T = tree.T
     M = B * T
@@ -472,6 +506,10 @@ def main():
             "B1_MHA32_L65536": {"us": round(amha_ms * 1e3, 2), "achieved": round(amha_gbs, 1), "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s", "frac": round(amha_gbs / HBM_PEAK_GBS, 4), "bytes": amha_b}},
         "prefix_sweep": sweep,
+        "tree_size_sweep": {"acceptance": "synthetic table: depth d in top-10 with probability 0.75 * 0.85^d, "
+                                          "ranks in proportion to 0.5^r (not from the pages)",
+                            "trees": "medusa_tree_from_acceptance (n - 1 most probable rank paths)",
+                            "sizes": tree_sweep},
         "fused_draft_verify": {"ms_per_step": round(fused_ms, 4), "steps_per_s": round(1e3 / fused_ms, 3),
                                "note": "heads on all 64 tree nodes in the step (M = 64), next candidates at the "
                                        "selected node; the reported step runs the heads on the selected node only"},

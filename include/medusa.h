@@ -189,6 +189,46 @@ int kv_compact(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, in
                const int32_t* accept_len, int32_t* seq_len, const int32_t* tree_tokens,
                int32_t* out_tokens, int max_new, int32_t* n_out, int32_t* err_flag, hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* Tree calibration                                                           */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * The static sparse tree from per-(depth, rank) acceptance rates (page
+ * "memory bandwidth bound (5) - Medusa", section 一.2: the tree is built ahead
+ * of time, keeping the probable candidate paths; the figure there relates the
+ * candidate count to the accepted length and the speed).  Reading, as the page
+ * gives no construction: the true token of depth d sits at rank r of head d's
+ * top-K with probability acc[d*K + r], ranks of one depth exclusive, depths
+ * independent; a path's probability is the product of acc along its ranks
+ * (multiplied from depth 0 up); a tree's expected accepted length is the sum of
+ * its paths' probabilities, which the n_nodes - 1 most probable paths maximise
+ * (ties: the shorter path, then the lexicographically smaller ranks).
+ *   acc        host, H*K doubles, each in [0, 1], each depth's sum <= 1
+ *   n_nodes    1..MEDUSA_MAX_TREE nodes, root included, <= 1 + sum_d K^d
+ *   ranks      host out, capacity (n_nodes - 1) * H: the paths' ranks, concatenated
+ *   offsets    host out, n_nodes entries: path i = ranks[offsets[i] .. offsets[i+1])
+ *              (the medusa_tree_create format), in selection order
+ *   expected   host out (nullable): the sum of the chosen path probabilities,
+ *              added in selection order
+ * Host only (no device call).  MEDUSA_ERR_ARG for bad sizes or a bad table.
+ */
+int medusa_tree_from_acceptance(const double* acc, int32_t H, int32_t K, int32_t n_nodes, int32_t* ranks,
+                                int32_t* offsets, double* expected);
+
+/*
+ * Teacher-forced hits of the heads, the measurement behind such a table: for
+ * every position t < N and head k < H with t + k + 2 < n_tokens,
+ *   positions[k] += 1;  counts[k*K + r] += (topk[(t*H + k)*K + r] == tokens[t + k + 2])
+ * (head k at the hidden state of tokens[t] predicts the token k + 1 places
+ * after the LM head's target tokens[t + 1]).
+ *   topk [N, H, K] int32, tokens [n_tokens] int32: device
+ *   counts [H*K], positions [H] int64: device, added to (the caller zeroes them)
+ * H*K <= 4096.  Counts are exact integers, independent of the launch shape.
+ */
+int medusa_head_hits(int N, int H, int K, const int32_t* topk, const int32_t* tokens, int n_tokens,
+                     int64_t* counts, int64_t* positions, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,7 @@ EXPORTED = [
     "medusa_forward_workspace_size", "medusa_forward", "medusa_prefill_workspace_size", "medusa_prefill",
     "medusa_step_workspace_size", "medusa_step", "medusa_step_graph_create", "medusa_graph_launch",
     "medusa_graph_destroy", "medusa_step_fused_workspace_size", "medusa_step_fused",
+    "medusa_tree_from_acceptance", "medusa_head_hits",
 ]
 
 
@@ -110,6 +111,8 @@ def _declare(lib):
         "medusa_step_fused_workspace_size": (_S, [C.POINTER(ModelDesc), _P, _I, _L]),
         "medusa_step_fused": (_I, [C.POINTER(ModelDesc), _P, _I, _I, _F, _F, _F, C.POINTER(StateDesc), _P, _L, _P,
                                    _S, _P]),
+        "medusa_tree_from_acceptance": (_I, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, C.POINTER(C.c_double)]),
+        "medusa_head_hits": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P]),
         "medusa_graph_launch": (_I, [_P, _P]),
         "medusa_graph_destroy": (_I, [_P]),
     }

@@ -210,3 +210,36 @@ def topk_rows(x, K):
     ws = L._ws(None, lib().medusa_topk_rows_workspace_size(M, V, K), x.device)
     check(lib().medusa_topk_rows(M, V, ptr(x), K, ptr(idx), ptr(val), ptr(ws), ws.numel(), stream_ptr()))
     return idx, val
+
+
+def tree_from_acceptance(acc, n_nodes):
+    """medusa_tree_from_acceptance: (choices in selection order, expected accepted length).
+
+    acc: [H, K] per-(depth, rank) acceptance rates (host array); host-only call."""
+    a = np.ascontiguousarray(np.asarray(acc, dtype=np.float64))
+    if a.ndim != 2:
+        raise L.MedusaError("tree_from_acceptance: acc must be [H, K]")
+    H, K = a.shape
+    n = int(n_nodes)
+    ranks = np.zeros(max(n - 1, 1) * H, np.int32)
+    offsets = np.zeros(max(n, 1), np.int32)
+    exp = C.c_double(0.0)
+    check(lib().medusa_tree_from_acceptance(a.ctypes.data, H, K, n, ranks.ctypes.data, offsets.ctypes.data,
+                                            C.byref(exp)))
+    choices = [tuple(int(r) for r in ranks[offsets[i]:offsets[i + 1]]) for i in range(n - 1)]
+    return choices, exp.value
+
+
+def head_hits(topk, tokens, counts=None, positions=None):
+    """medusa_head_hits on device tensors: topk [N, H, K] int32, tokens [n] int32.
+
+    Adds to counts [H, K] / positions [H] (int64, zeroed here when not given)."""
+    torch = _torch()
+    N, H, K = topk.shape
+    if counts is None:
+        counts = torch.zeros((H, K), dtype=torch.int64, device=topk.device)
+    if positions is None:
+        positions = torch.zeros(H, dtype=torch.int64, device=topk.device)
+    check(lib().medusa_head_hits(N, H, K, ptr(topk), ptr(tokens), tokens.numel(), ptr(counts), ptr(positions),
+                                 stream_ptr()))
+    return counts, positions

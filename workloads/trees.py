@@ -15,7 +15,7 @@ import itertools
 import numpy as np
 
 __all__ = ["PAGE_TREE_CHOICES", "TWO_HEAD_CHOICES", "seeded_tree_choices", "chain_choices",
-           "choices_to_arrays"]
+           "choices_to_arrays", "acceptance_table"]
 
 PAGE_TREE_CHOICES = [
     (0,), (0, 0), (1,), (0, 1), (0, 0, 0), (1, 0), (2,), (0, 2), (0, 0, 1), (0, 3), (3,),
@@ -64,3 +64,12 @@ def choices_to_arrays(choices):
         ranks.extend(int(r) for r in c)
         offsets.append(len(ranks))
     return np.asarray(ranks, dtype=np.int32), np.asarray(offsets, dtype=np.int32)
+
+
+def acceptance_table(H, K, top=0.75, depth_decay=0.85, rank_ratio=0.5):
+    """Synthetic per-(depth, rank) acceptance rates [H, K] (the pages print none):
+    depth d's true token is in the top-K with probability top * depth_decay**d,
+    split over the ranks in proportion to rank_ratio**r."""
+    w = rank_ratio ** np.arange(K, dtype=np.float64)
+    cover = top * depth_decay ** np.arange(H, dtype=np.float64)
+    return cover[:, None] * (w / w.sum())[None, :]
