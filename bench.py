@@ -28,6 +28,13 @@ Also measured (same JSON line):
                  medusa_heads_topk on the hidden states of every node of 8 sequences'
                  64-node trees (512 rows: the heads applied inside the verify forward),
                  against the 2.5 PFLOP/s dense bf16 peak
+  tree_attention_sweep
+                 the attention kernel alone at prefixes 1k..64k, batch 1 and 8
+  heads_topk_candidates
+                 heads + top-10 + candidate expansion at batch 1 and 8 (1.18 GB of head
+                 weights per call), against 8 TB/s
+  kv_compact     the compaction call at batch 8, prefix 65536 (one layer)
+  tiny_fp32_step the 2-layer fp32 model's verify step (launch-bound): steps/s, tok/s
   cpu_baseline   the oracle on the host cores on a bounded sample of the same step
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -464,6 +471,84 @@ def main():
     heads_tfs = heads_flop / (heads_ms * 1e-3) / 1e12
     log("heads on all tree nodes (M %d): %.1f us, %.1f TFLOP/s" % (Bh, heads_ms * 1e3, heads_tfs))
 
+    # ---- tree attention alone over prefixes 1k..64k at batch 1 and 8 (32/8 heads)
+    attn_sweep = {}
+    for Bc in (1, 8):
+        for Ls in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+            if Bc == 8 and Ls == 65536:
+                ms_, b_ = a64_ms, a64_b
+            else:
+                ms_, b_ = attn_case(Bc, Ls, max(5, args.attn_reps // 2))
+            g_ = b_ / (ms_ * 1e-3) / 1e9
+            attn_sweep["B%d_L%d" % (Bc, Ls)] = {"us": round(ms_ * 1e3, 2), "achieved": round(g_, 1),
+                                                "frac": round(g_ / HBM_PEAK_GBS, 4), "bytes": b_}
+    log("tree_attention sweep: " + ", ".join("%s %.1f us" % (k, v["us"]) for k, v in attn_sweep.items()))
+
+    # ---- heads + top-K + candidates at batch 1 and 8 (the heads' 1.18 GB of weights streamed once)
+    heads_b = {}
+    tree10 = api.Tree(seeded_tree_choices(0), K=10)  # the same tree on a top-10 stride
+    W1, W2 = heads["W1"], heads["W2"]
+    hbytes = W1.numel() * 2 + W2.numel() * 2
+    for Bc in (1, 8):
+        hb = torch_normal((Bc, cfg.d), 1.0, 78, dev, torch.bfloat16)
+        hidx_b = torch.empty((Bc, cfg.n_medusa, 10), dtype=torch.int32, device=dev)
+        hws_b = torch.empty(max(1, lib().medusa_heads_topk_workspace_size(1, Bc, cfg.d, cfg.vocab, cfg.n_medusa, 10)),
+                            dtype=torch.uint8, device=dev)
+        root_b = torch.zeros(Bc, dtype=torch.int32, device=dev)
+        seq_b = torch.full((Bc,), args.prefix, dtype=torch.int32, device=dev)
+
+        def heads_cand():
+            api.medusa_heads_topk(hb, W1, W2, 10, topk_idx=hidx_b, ws=hws_b)
+            api.tree_build_candidates(tree10, root_b, hidx_b, seq_b)
+
+        for _ in range(2):
+            heads_cand()
+        torch.cuda.synchronize()
+        with Timer() as thb:
+            for _ in range(10):
+                heads_cand()
+        ms_ = thb.ms() / 10
+        g_ = hbytes / (ms_ * 1e-3) / 1e9
+        heads_b["B%d" % Bc] = {"us": round(ms_ * 1e3, 2), "achieved": round(g_, 1), "unit": "GB/s",
+                               "frac": round(g_ / HBM_PEAK_GBS, 4), "bytes": hbytes}
+    log("heads + top-K + candidates: " + ", ".join("%s %.1f us" % (k, v["us"]) for k, v in heads_b.items()))
+
+    # ---- KV compaction after acceptance: one layer, batch 8, 8 KV heads, prefix 65536,
+    # accepted length a ~ U{0..4} on a seeded leaf path long enough for it
+    rng_c = np.random.default_rng(5)
+    Bc, Lc = 8, 65536
+    Kc5 = torch.zeros((1, Bc, 8, Lc + 128, Dh), dtype=torch.bfloat16, device=dev)
+    Vc5 = torch.zeros_like(Kc5)
+    Kt5 = torch_normal((1, Bc, 8, T, Dh), 1.0, 90, dev, torch.bfloat16)
+    Vt5 = torch_normal((1, Bc, 8, T, Dh), 1.0, 91, dev, torch.bfloat16)
+    best_np = rng_c.integers(0, tree.P, Bc)
+    acc_np = np.array([rng_c.integers(0, min(5, int(tree.path_len[b_]))) for b_ in best_np])
+    best5 = torch.from_numpy(best_np.astype(np.int32)).to(dev)
+    acc5 = torch.from_numpy(acc_np.astype(np.int32)).to(dev)
+    seq5_0 = torch.full((Bc,), Lc, dtype=torch.int32, device=dev)
+    seq5 = seq5_0.clone()
+    tt5 = torch.zeros((Bc, T), dtype=torch.int32, device=dev)
+
+    def compact5():
+        seq5.copy_(seq5_0)
+        api.kv_compact(tree, Kc5, Vc5, Kt5, Vt5, best5, acc5, seq5, tt5)
+
+    for _ in range(3):
+        compact5()
+    torch.cuda.synchronize()
+    with Timer() as tc5:
+        for _ in range(20):
+            compact5()
+    compact_us = tc5.ms() / 20 * 1e3
+    compact_bytes = int(2 * 2 * 8 * Dh * 2 * int((acc_np + 1).sum()))
+    log("kv_compact B8 L65536 (1 layer): %.1f us per call (with the length reset)" % compact_us)
+    del Kc5, Vc5
+    torch.cuda.empty_cache()
+
+    # ---- the tiny fp32 step (2-layer decoder, d 64, 2 heads, the 2-head tree): launch-bound
+    tiny = tiny_step_rate(dev)
+    log("tiny fp32 step: %.1f us, %.0f steps/s" % (tiny["us_per_step"], tiny["steps_per_s"]))
+
     # ---- oracle on the host cores, bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
@@ -518,9 +603,50 @@ def main():
             "rows": Bh, "bound": "mfma", "us": round(heads_ms * 1e3, 2), "achieved": round(heads_tfs, 1),
             "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(heads_tfs / MFMA_PEAK_TFS, 4),
             "flop": heads_flop},
+        "tree_attention_sweep": {"heads": "32 query / 8 KV heads x 128, 64-node tree, bf16", "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "cases": attn_sweep},
+        "heads_topk_candidates": {"kernels": "medusa_heads_topk (W1, W2 products + top-10) + tree_build_candidates",
+                                  "bound": "hbm", "peak": HBM_PEAK_GBS, "cases": heads_b},
+        "kv_compact": {"case": "1 layer, batch 8, 8 KV heads x 128, prefix 65536, a ~ U{0..4}",
+                       "us_per_call": round(compact_us, 2), "bytes_moved": compact_bytes,
+                       "note": "launch-bound: the time includes a 32-byte length reset"},
+        "tiny_fp32_step": tiny,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def tiny_step_rate(dev, steps=16):
+    """The tiny fp32 Medusa step (2-layer decoder, d 64, 4 x 16 heads, SwiGLU 128, V 512,
+    2 Medusa heads, the 2-head tree, greedy) after a 32-token prefill: microseconds per
+    step (HIP events, eager launches) and accepted tokens per step."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import GREEDY
+    from speculative_decoding_heads_amd.model import Model, State, prefill, step, step_workspace_size
+    from workloads import TWO_HEAD_CHOICES, TinyConfig, prompt_tokens, tiny_model
+    params, heads = tiny_model(0)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    P = dict(params)
+    P["embed"], P["final_norm"], P["lm_head"] = up(params["embed"]), up(params["final_norm"]), up(params["lm_head"])
+    P["layers"] = [{k: up(v) for k, v in l.items()} for l in params["layers"]]
+    model = Model(P, {k: up(v) for k, v in heads.items()}, max_pos=512)
+    tree = api.Tree(TWO_HEAD_CHOICES)
+    prompt = up(prompt_tokens(100, 1, TinyConfig.prompt_len, TinyConfig.vocab).astype(np.int32))
+    st = State(model, 1, 256, 4 * steps)
+    ws = torch.empty(max(1, step_workspace_size(model, tree, 1, 256)), dtype=torch.uint8, device=dev)
+    prefill(model, st, prompt)
+    for _ in range(3):
+        step(model, tree, st, GREEDY, L_hint=256, ws=ws)
+    torch.cuda.synchronize()
+    n0 = int(st.n_out[0])
+    with Timer() as t:
+        for _ in range(steps):
+            step(model, tree, st, GREEDY, L_hint=256, ws=ws)
+    us = t.ms() / steps * 1e3
+    toks = (int(st.n_out[0]) - n0) / steps
+    return {"us_per_step": round(us, 2), "steps_per_s": round(1e6 / us, 1), "accepted_tokens_per_step": round(toks, 3),
+            "tok_per_s": round(1e6 / us * toks, 1), "bound": "launch latency"}
 
 
 def make_gate_up(model, cfg, NL, M, dev):
