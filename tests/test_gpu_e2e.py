@@ -14,7 +14,7 @@ from oracle.heads import medusa_heads_logits, topk_desc
 from oracle.loop import medusa_generate
 from oracle.posterior import GREEDY, TYPICAL, evaluate_posterior_one
 from oracle.tree import tree_buffers
-from workloads import PAGE_TREE_CHOICES, TWO_HEAD_CHOICES, TinyConfig, prompt_tokens, tiny_model
+from workloads import PAGE_TREE_CHOICES, TWO_HEAD_CHOICES, TinyConfig, prompt_tokens, seeded_tree_choices, tiny_model
 
 from _gpu import assert_close, say, to_dev, to_np
 
@@ -226,17 +226,23 @@ def _small_bf16_model(seed, heads_kv_dim=(8, 4, 64)):
 # projection + rotary epilogue (64 tree rows x batch 2 = 128 product rows);
 # at batch 1 (64 rows, one activation tile) MHA with head sizes 128 and 64
 # takes the 48-row q/K/V workgroups
-@pytest.mark.parametrize("heads_kv_dim,B", [((8, 4, 64), 2), ((4, 4, 128), 2), ((4, 4, 128), 1), ((8, 8, 64), 1)])
-def test_bf16_forward_vs_oracle(dev, heads_kv_dim, B):
+# small trees (9 and 24 nodes: 9 to 48 product rows) take the same 64-row-tile
+# kernels with the rows past M re-reading the last one
+@pytest.mark.parametrize("heads_kv_dim,B,tree_name", [((8, 4, 64), 2, "page"), ((4, 4, 128), 2, "page"),
+                                                      ((4, 4, 128), 1, "page"), ((8, 8, 64), 1, "page"),
+                                                      ((4, 4, 128), 1, "two_head"), ((8, 4, 64), 2, "seeded24")])
+def test_bf16_forward_vs_oracle(dev, heads_kv_dim, B, tree_name):
     import torch
     from speculative_decoding_heads_amd import api
     from speculative_decoding_heads_amd.model import Model
-    say("e2e bf16 forward vs oracle", heads_kv_dim, "batch", B)
+    say("e2e bf16 forward vs oracle", heads_kv_dim, "batch", B, tree_name)
     (params, heads), Cfg = _small_bf16_model(3, heads_kv_dim)
     P, H = _upload(params, heads, torch.bfloat16, dev)
     model = Model(P, H, max_pos=1024)
-    tree = api.Tree(PAGE_TREE_CHOICES)
-    ot = tree_buffers(PAGE_TREE_CHOICES)
+    choices = {"page": PAGE_TREE_CHOICES, "two_head": TWO_HEAD_CHOICES,
+               "seeded24": seeded_tree_choices(3, n_nodes=23)}[tree_name]
+    tree = api.Tree(choices)
+    ot = tree_buffers(choices)
     rng = np.random.default_rng(4)
     L, Lmax = 150, 192
     NL, Hkv, Dh = Cfg.n_layers, Cfg.n_kv_heads, Cfg.head_dim
@@ -244,7 +250,7 @@ def test_bf16_forward_vs_oracle(dev, heads_kv_dim, B):
     Kc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
     Vc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
     seq = np.array([L, L - 37][:B], np.int32)
-    toks = rng.integers(0, Cfg.vocab, (B, 64)).astype(np.int32)
+    toks = rng.integers(0, Cfg.vocab, (B, ot["T"])).astype(np.int32)
     pos = (seq[:, None] + ot["depth"][None, :]).astype(np.int32)
     d = lambda x: torch.from_numpy(x).to(dev)
     logits, h, Kt, Vt = model.forward(d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev), to_dev(Vc, torch.bfloat16, dev),
