@@ -230,7 +230,10 @@ def test_heads_topk_fp32_small(dev):
                                    # streaming path with three-wave 96-row workgroup tiles (ragged last tile)
                                    (64, 20000, 256),
                                    # streaming path, 128-row workgroup tiles; 48 rows (clamped A rows)
-                                   (64, 32000, 256), (48, 5000, 1024)])
+                                   (64, 32000, 256), (48, 5000, 1024),
+                                   # few rows with K % 64 != 0: the register-staged 64-row-tile kernel,
+                                   # rows past M re-reading the last one
+                                   (1, 3000, 1056), (5, 4096, 96), (17, 700, 1056)])
 def test_gemm_bf16(dev, M, N, K):
     import torch
     from speculative_decoding_heads_amd import api
