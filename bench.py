@@ -40,6 +40,8 @@ Also measured (same JSON line):
 python bench.py [--gpus 1] [--steps K] [--warmup W]
 python bench.py --roofline-only      the dominant-kernel launches and a 256 MiB copy
                                      (counter calibration) only, for rocprofv3 --pmc
+python bench.py --attn-traffic-only  the batch-8 / prefix-65536 attention launches and the
+                                     256 MiB copy only, for rocprofv3 --pmc
 python bench.py --traffic-from FETCH_DIR WRITE_DIR
                                      turn the two counter runs into the traffic file
 """
@@ -75,6 +77,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--attn-reps", type=int, default=20)
     p.add_argument("--roofline-only", action="store_true")
+    p.add_argument("--attn-traffic-only", action="store_true")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     p.add_argument("--sweep", type=str, default="4096,16384,65536",
                    help="longer prefixes at which the same step is also timed ('' for none)")
@@ -185,6 +188,9 @@ def main():
     cfg = SevenBConfig
     NL = args.layers
     lib()
+    if args.attn_traffic_only:
+        attn_traffic_run(dev)
+        return
     log("generating %d-layer 7B-shaped weights on device" % NL)
     params, heads = model_weights_torch(cfg, 1, dev, torch.bfloat16, n_layers=NL)
     sample_layers = [{k: v for k, v in params["layers"][i].items()} for i in range(min(4, NL))]
@@ -614,6 +620,39 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def attn_traffic_run(dev):
+    """For rocprofv3 --pmc: three launches of the attention kernel at batch 8, 32/8 heads x 128,
+    prefix 65536, the seeded 64-node tree (one K/V set, 2 147 483 648 cache bytes), then three
+    256 MiB row copies (gather_rows_kernel) as the counter calibration."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import check, lib, ptr, stream_ptr
+    from workloads import seeded_tree_choices, torch_normal
+    tree = api.Tree(seeded_tree_choices(0))
+    Bc, Hkv, L, Dh, T = 8, 8, 65536, 128, tree.T
+    q = torch_normal((Bc, T, 32, Dh), 1.0, 11, dev, torch.bfloat16)
+    Kc = torch_normal((Bc, Hkv, L, Dh), 1.0, 20, dev, torch.bfloat16)
+    Vc = torch_normal((Bc, Hkv, L, Dh), 1.0, 40, dev, torch.bfloat16)
+    Kt = torch_normal((Bc, Hkv, T, Dh), 1.0, 60, dev, torch.bfloat16)
+    Vt = torch_normal((Bc, Hkv, T, Dh), 1.0, 61, dev, torch.bfloat16)
+    seq = torch.full((Bc,), L, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    aws = torch.empty(max(1, api.tree_attention_workspace_size(1, Bc, T, 32, Hkv, Dh, L)), dtype=torch.uint8,
+                      device=dev)
+    for _ in range(3):
+        api.tree_attention(q, Kc, Vc, seq, Kt, Vt, tree, Dh ** -0.5, out=out, ws=aws)
+    torch.cuda.synchronize()
+    rows = COPY_BYTES // 8192
+    src = torch.ones((rows, 1, 2048), dtype=torch.float32, device=dev)
+    dst = torch.empty((rows, 2048), dtype=torch.float32, device=dev)
+    sel = torch.zeros(rows, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        check(lib().medusa_gather_rows(0, rows, 1, 2048, ptr(src), ptr(sel), ptr(dst), stream_ptr()))
+    torch.cuda.synchronize()
+    nbytes = Bc * Hkv * L * Dh * 2 * 2 + Bc * Hkv * T * Dh * 2 * 2 + 2 * Bc * T * 32 * Dh * 2
+    print(json.dumps({"attn_algorithmic_bytes": nbytes, "copy_bytes": COPY_BYTES}), flush=True)
 
 
 def tiny_step_rate(dev, steps=16):
