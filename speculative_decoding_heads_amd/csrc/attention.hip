@@ -194,11 +194,35 @@ struct MfmaPlan {
   size_t ws_o_bytes, ws_ml_bytes;
 };
 
+MfmaPlan mfma_plan_nw(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint, int nw);
+
+// Waves per workgroup: the largest of 8, 4, 2 whose plan puts >= 256
+// workgroups on the chip (one per CU), else the one with the most workgroups
+// (larger on a tie).  Fewer waves mean 32-row chunks of fewer query rows and so
+// more workgroups when batch x KV heads is small (batch 1 with shared KV heads:
+// 8 x 8 splits at 8 waves, 256 workgroups at 2); where 8 waves already fill the
+// chip they measure faster.  MEDUSA_ATTN_WAVES = 2 | 4 | 8 forces a count.
 MfmaPlan mfma_plan(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint) {
+  const int forced = attn_stream_waves_forced();
+  if (forced) return mfma_plan_nw(B, T, Hq, Hkv, Dh, L_hint, forced);
+  MfmaPlan best{};
+  int64_t best_wgs = -1;
+  for (int nw : {8, 4, 2}) {
+    const MfmaPlan p = mfma_plan_nw(B, T, Hq, Hkv, Dh, L_hint, nw);
+    const int64_t wgs = (int64_t)p.n_splits * Hkv * B * p.n_rchunks;
+    if (wgs >= 256) return p;
+    if (wgs > best_wgs) {
+      best = p;
+      best_wgs = wgs;
+    }
+  }
+  return best;
+}
+
+MfmaPlan mfma_plan_nw(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint, int nw) {
   MfmaPlan p;
   const int R = T * (Hq / Hkv);
-  p.nw = attn_stream_waves();
-  const int nw = p.nw;
+  p.nw = nw;
   const int rows_wg = 32 * nw;
   p.n_rchunks = (R + rows_wg - 1) / rows_wg;
   const int64_t tiles = (L_hint + ATTN_KT - 1) / ATTN_KT;

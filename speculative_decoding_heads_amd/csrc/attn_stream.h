@@ -6,8 +6,8 @@ namespace medusa {
 
 constexpr int ATTN_KT = 64;  // keys per tile
 
-// Waves per workgroup (32 query rows each).
-int attn_stream_waves();
+// Waves per workgroup (32 query rows each) forced by MEDUSA_ATTN_WAVES (2, 4 or 8), else 0.
+int attn_stream_waves_forced();
 
 // nw waves per workgroup (2, 4 or 8); grid = (n_splits, Hkv, B * n_rchunks)
 // with n_rchunks = ceil(R / (32 * nw)); ws_o / ws_ml used only when n_splits > 1.

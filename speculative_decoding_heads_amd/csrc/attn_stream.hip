@@ -456,13 +456,13 @@ __global__ __launch_bounds__(NW * 64) void attn_lds_kernel(
 // Waves per workgroup: 8 (the waves past the rows of a KV head still stream
 // tiles in, which keeps more loads in flight); MEDUSA_ATTN_WAVES = 2 | 4 | 8
 // forces a width for tuning runs.
-int attn_stream_waves() {
+int attn_stream_waves_forced() {
   static const int forced = [] {
     const char* e = getenv("MEDUSA_ATTN_WAVES");
     const int v = e ? atoi(e) : 0;
     return v == 2 || v == 4 || v == 8 ? v : 0;
   }();
-  return forced ? forced : 8;
+  return forced;
 }
 
 template <int NW, int NBUF>
