@@ -200,7 +200,7 @@ def main():
         for k in ("wq", "wk", "wv", "w_gate", "w_up"):
             l[k] = None
     torch.cuda.empty_cache()
-    tree = api.Tree(seeded_tree_choices(0))
+    tree = api.Tree(seeded_tree_choices(0), K=10)  # the heads' top-10 as the tree's rank stride
     B = 1
     gate_up = make_gate_up(model, cfg, NL, tree.T * B, dev)
     if args.roofline_only:

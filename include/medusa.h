@@ -146,8 +146,9 @@ int tree_build_candidates(const medusa_tree* t, int B, int H, int K, const int32
  *   anc    [T]                  uint64  device; bit j of anc[i] = node j visible to i
  *   out    [B, T, Hq, Dh]       dtype
  *   L_hint  host upper bound of max(seq_len) used to size the split-KV grid (<= Lmax)
- * T <= 64.  fp32: any Dh <= 256 (deterministic key order by absolute position).
- * bf16: Dh in {64, 128} use the MFMA kernel; other Dh <= 256 the generic kernel.
+ * T <= 64.  bf16 with Dh in {64, 128}: the MFMA kernel; fp32, and bf16 with
+ * any other Dh <= 128: the generic kernel (deterministic key order by absolute
+ * position); Dh > 128 outside {64, 128} returns MEDUSA_ERR_UNSUPPORTED.
  * Also serves chain-masked prefill chunks (anc = lower triangle) and T = 1 decode.
  */
 size_t tree_attention_workspace_size(int dtype, int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint);

@@ -128,6 +128,32 @@ size_t medusa_forward_workspace_size(const medusa_model* m, int B, int T, int64_
 int medusa_forward(const medusa_model* m, int B, int T, const int32_t* tokens, const int32_t* pos, const void* Kc,
                    const void* Vc, int64_t Lmax, int64_t L_hint, const int32_t* seq_len, void* Kt, void* Vt,
                    const uint64_t* anc, float* logits, void* h, void* ws, size_t ws_bytes, hipStream_t stream);
+/*
+ * medusa_forward that also copies each stage's output into caller buffers, for
+ * stage-by-stage checks against a reference (every pointer nullable, device,
+ * caller-owned, in the model's dtype; rows are the B*T new tokens, b-major):
+ *   x     [n_layers + 1, B*T, d]   residual stream entering layer l (slot 0: the
+ *                                  embedding rows); slot n_layers: leaving the last
+ *   xn    [n_layers, B*T, d]       the attention RMSNorm's output of layer l
+ *   q     [n_layers, B*T, Hq*Dh]   rotated queries ([B, T, Hq, Dh] per layer)
+ *   attn  [n_layers, B*T, Hq*Dh]   tree-attention output
+ *   x_mid [n_layers, B*T, d]       residual stream after the attention block
+ *   act   [n_layers, B*T, F]       SwiGLU product feeding the down projection
+ * Same kernels and results as medusa_forward, plus one device copy per buffer
+ * and layer.
+ */
+typedef struct medusa_trace {
+  void* x;
+  void* xn;
+  void* q;
+  void* attn;
+  void* x_mid;
+  void* act;
+} medusa_trace;
+int medusa_forward_trace(const medusa_model* m, int B, int T, const int32_t* tokens, const int32_t* pos,
+                         const void* Kc, const void* Vc, int64_t Lmax, int64_t L_hint, const int32_t* seq_len,
+                         void* Kt, void* Vt, const uint64_t* anc, float* logits, void* h, const medusa_trace* trace,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Generation state of B sequences (all device buffers, caller-owned):
@@ -176,6 +202,10 @@ int medusa_prefill(const medusa_model* m, int B, int S, const int32_t* prompt, m
  * One verify iteration for B sequences sharing tree t:
  *   Medusa heads + top-K on h_sel -> candidates -> forward of the T tree tokens
  *   -> acceptance -> KV compaction + token append -> h_sel, root for the next step.
+ * best, accept_len and sel_node are written for every sequence; root and h_sel
+ * change only for a sequence that appended all its accepted tokens, so one whose
+ * cache or output was full (err set) or that is finished keeps the state its
+ * cache and length describe.
  * L_hint: host upper bound of the sequence lengths during this step (<= Lmax).
  * topk_override [B, H, K] (nullable): when non-null, used instead of the heads'
  * top-K (forced-acceptance tests).

@@ -15,7 +15,7 @@ path: both sides only share the seeded input generators in ``workloads``.
 
 Modules
 -------
-numerics    bfloat16 round-to-nearest-even, SiLU, stable softmax (fp64)
+numerics    bfloat16 round-to-nearest-even, SiLU, first-index argmax (fp64)
 tree        static sparse-tree buffers from rank-path choices
 heads       Medusa residual heads, top-K and the root argmax
 candidates  flat candidate list -> tree tokens, positions, cartesian paths

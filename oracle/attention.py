@@ -30,12 +30,13 @@ def attention_slice(q, Kp, Vp, Kt, Vt, anc, scale):
     L = Kp.shape[0]
     T, G, Dh = q.shape
     visible = np.concatenate([np.ones((T, L), dtype=bool), np.asarray(anc, dtype=bool)], axis=1)
-    s = np.einsum("tgd,nd->tgn", q, K) * scale
+    # scores of every (node, head) row against every key: one matrix product
+    s = (q.reshape(T * G, Dh) @ K.T).reshape(T, G, -1) * scale
     s = np.where(visible[:, None, :], s, -np.inf)
     m = np.max(s, axis=-1, keepdims=True)
     p = np.exp(s - m)
     p /= np.sum(p, axis=-1, keepdims=True)
-    return np.einsum("tgn,nd->tgd", p, V)
+    return (p.reshape(T * G, -1) @ V).reshape(T, G, Dh)
 
 
 def tree_attention(q, Kc, Vc, seq_len, Kt, Vt, anc, scale):

@@ -50,6 +50,72 @@ def _mm(x, W, mm_dtype):
     return (np.asarray(x, mm_dtype) @ np.asarray(W, mm_dtype).T).astype(np.float64)
 
 
+def qkv_rotary(params, p, xn, pos, bf16=False, mm_dtype=np.float64):
+    """Projections of the attention-normed rows xn [B, T, d] and the rotary embedding:
+    (q [B, T, Hq, Dh], K [B, Hkv, T, Dh], V [B, Hkv, T, Dh])."""
+    rb = round_bf16 if bf16 else (lambda v: v)
+    Hq, Hkv, Dh = params["n_heads"], params["n_kv_heads"], params["head_dim"]
+    B, T = xn.shape[:2]
+    q = _mm(xn, p["wq"], mm_dtype).reshape(B, T, Hq, Dh)
+    k = _mm(xn, p["wk"], mm_dtype).reshape(B, T, Hkv, Dh)
+    v = _mm(xn, p["wv"], mm_dtype).reshape(B, T, Hkv, Dh)
+    q = rb(rope(q, pos, params["rope_theta"]))
+    k = rb(rope(k, pos, params["rope_theta"]))
+    v = rb(v)
+    return q, k.transpose(0, 2, 1, 3), v.transpose(0, 2, 1, 3)
+
+
+def attention_residual(p, x, att, bf16=False, mm_dtype=np.float64):
+    """Residual stream after the attention block: x + att W_o (att [B, T, Hq*Dh])."""
+    rb = round_bf16 if bf16 else (lambda v: v)
+    B, T = x.shape[:2]
+    return rb(np.asarray(x, np.float64) + _mm(np.asarray(att).reshape(B, T, -1), p["wo"], mm_dtype))
+
+
+def ffn_act(params, p, x_mid, bf16=False, mm_dtype=np.float64):
+    """SwiGLU product of the FFN sub-layer: SiLU(gate) * up of the RMS-normed stream x_mid."""
+    rb = round_bf16 if bf16 else (lambda v: v)
+    xn2 = rb(rmsnorm(x_mid, p["ffn_norm"], params["norm_eps"]))
+    return rb(silu(_mm(xn2, p["w_gate"], mm_dtype)) * _mm(xn2, p["w_up"], mm_dtype))
+
+
+def down_residual(p, x_mid, act, bf16=False, mm_dtype=np.float64):
+    """Residual stream leaving the layer: x_mid + act W_down."""
+    rb = round_bf16 if bf16 else (lambda v: v)
+    return rb(np.asarray(x_mid, np.float64) + _mm(act, p["w_down"], mm_dtype))
+
+
+def decoder_layer(params, p, x, pos, cacheK, cacheV, seq_len, anc, bf16=False, mm_dtype=np.float64):
+    """One pre-norm block over the new tokens' residual stream.
+
+    p: the layer's weights; x [B, T, d] the residual stream entering the layer;
+    pos [B, T]; cacheK, cacheV [B, Hkv, Lmax, Dh] this layer's cache with
+    seq_len[b] valid rows; anc [T, T] bool visibility among the new tokens.
+    Returns (x leaving the layer [B, T, d], K, V of the new tokens [B, Hkv, T, Dh]).
+    """
+    rb = round_bf16 if bf16 else (lambda v: v)
+    x = np.asarray(x, np.float64)
+    xn = rb(rmsnorm(x, p["attn_norm"], params["norm_eps"]))
+    q, Kt, Vt = qkv_rotary(params, p, xn, pos, bf16, mm_dtype)
+    att = rb(tree_attention(q, cacheK, cacheV, seq_len, Kt, Vt, anc, 1.0 / np.sqrt(params["head_dim"])))
+    x = attention_residual(p, x, att, bf16, mm_dtype)
+    x = down_residual(p, x, ffn_act(params, p, x, bf16, mm_dtype), bf16, mm_dtype)
+    return x, Kt, Vt
+
+
+def final_logits(params, x, bf16=False, mm_dtype=np.float64):
+    """Final RMSNorm of the residual stream x [B, T, d] and the LM head: (logits, h)."""
+    rb = round_bf16 if bf16 else (lambda v: v)
+    h = rb(rmsnorm(x, params["final_norm"], params["norm_eps"]))
+    return _mm(h, params["lm_head"], mm_dtype), h
+
+
+def embed_tokens(params, tokens, bf16=False):
+    """Residual stream entering the first layer: the embedding rows of the tokens [B, T]."""
+    rb = round_bf16 if bf16 else (lambda v: v)
+    return rb(np.asarray(params["embed"], np.float64)[np.asarray(tokens, dtype=np.int64)])
+
+
 def forward(params, tokens, pos, cacheK, cacheV, seq_len, anc, bf16=False, mm_dtype=np.float64,
             layers=None):
     """Run the decoder over new tokens.
@@ -60,37 +126,17 @@ def forward(params, tokens, pos, cacheK, cacheV, seq_len, anc, bf16=False, mm_dt
     ``layers`` limits the run to the first n layers (sampled checks); logits are
     then those of the truncated stack.
     """
-    rb = round_bf16 if bf16 else (lambda v: v)
-    Hq, Hkv, Dh = params["n_heads"], params["n_kv_heads"], params["head_dim"]
-    eps, theta = params["norm_eps"], params["rope_theta"]
     tokens = np.asarray(tokens, dtype=np.int64)
     B, T = tokens.shape
-    x = rb(np.asarray(params["embed"], np.float64)[tokens])
+    Hkv, Dh = params["n_kv_heads"], params["head_dim"]
+    x = embed_tokens(params, tokens, bf16)
     NL = len(params["layers"]) if layers is None else layers
     Knew = np.zeros((NL, B, Hkv, T, Dh))
     Vnew = np.zeros((NL, B, Hkv, T, Dh))
-    scale = 1.0 / np.sqrt(Dh)
     for li in range(NL):
-        p = params["layers"][li]
-        xn = rb(rmsnorm(x, p["attn_norm"], eps))
-        q = _mm(xn, p["wq"], mm_dtype).reshape(B, T, Hq, Dh)
-        k = _mm(xn, p["wk"], mm_dtype).reshape(B, T, Hkv, Dh)
-        v = _mm(xn, p["wv"], mm_dtype).reshape(B, T, Hkv, Dh)
-        q = rb(rope(q, pos, theta))
-        k = rb(rope(k, pos, theta))
-        v = rb(v)
-        Kt = k.transpose(0, 2, 1, 3)
-        Vt = v.transpose(0, 2, 1, 3)
-        Knew[li], Vnew[li] = Kt, Vt
-        att = rb(tree_attention(q, cacheK[li], cacheV[li], seq_len, Kt, Vt, anc, scale))
-        x = rb(x + _mm(att.reshape(B, T, Hq * Dh), p["wo"], mm_dtype))
-        xn2 = rb(rmsnorm(x, p["ffn_norm"], eps))
-        g = _mm(xn2, p["w_gate"], mm_dtype)
-        u = _mm(xn2, p["w_up"], mm_dtype)
-        act = rb(silu(g) * u)
-        x = rb(x + _mm(act, p["w_down"], mm_dtype))
-    h = rb(rmsnorm(x, params["final_norm"], eps))
-    logits = _mm(h, params["lm_head"], mm_dtype)
+        x, Knew[li], Vnew[li] = decoder_layer(params, params["layers"][li], x, pos, cacheK[li], cacheV[li],
+                                              seq_len, anc, bf16, mm_dtype)
+    logits, h = final_logits(params, x, bf16, mm_dtype)
     return logits, h, Knew, Vnew
 
 

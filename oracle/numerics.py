@@ -1,4 +1,4 @@
-"""Scalar helpers of the oracle: bf16 rounding, SiLU, softmax (all fp64).
+"""Scalar helpers of the oracle: bf16 rounding, SiLU, first-index argmax (fp64).
 
 Test infrastructure only (see ``oracle/__init__``).
 """
@@ -24,14 +24,6 @@ def silu(x):
     """SiLU(x) = x * sigmoid(x), as used inside the Medusa head residual block."""
     x = np.asarray(x, dtype=np.float64)
     return x / (1.0 + np.exp(-x))
-
-
-def softmax(x, axis=-1):
-    """Numerically stable softmax in float64."""
-    x = np.asarray(x, dtype=np.float64)
-    m = np.max(x, axis=axis, keepdims=True)
-    e = np.exp(x - m)
-    return e / np.sum(e, axis=axis, keepdims=True)
 
 
 def argmax_first(x, axis=-1):

@@ -49,11 +49,16 @@ def typical_node_stats(logits_row, temperature, eps, delta):
 
 
 def evaluate_posterior_one(tree, logits, tree_tokens, mode, temperature=0.0, eps=0.09, delta=0.3,
-                           decide_dtype=np.float32):
+                           decide_dtype=np.float32, flip=()):
     """One sequence.  logits [T, V], tree_tokens [T].
 
     Returns dict(best, accept_len, sel, next_root, acc [P], lik [P] (typical),
-    margins: list of per-decision margins used to spot near-ties).
+    margins: list of per-decision margins used to spot near-ties, node_margin [T]:
+    the relative margin |q - thr| / thr of the typical decision on each node's
+    candidate, inf where none is taken).
+    ``flip``: tree nodes whose accept decision is inverted -- a test hook that
+    shows whether one decision lying within rounding of its threshold accounts
+    for a difference from another implementation.
     """
     logits = np.asarray(logits, dtype=np.float64)
     tree_tokens = np.asarray(tree_tokens, dtype=np.int64)
@@ -68,13 +73,16 @@ def evaluate_posterior_one(tree, logits, tree_tokens, mode, temperature=0.0, eps
         stats = [typical_node_stats(logits[u], temperature, eps, delta) for u in range(T)]
     acc = np.zeros(P, dtype=np.int64)
     lik = np.zeros(P, dtype=np.float64)
+    node_margin = np.full(T, np.inf)
+    flip = set(int(c) for c in flip)
     for p in range(P):
         n = 0
         for j in range(1, D + 1):
             if j >= path_len[p]:
                 break  # padded slot: never accepted
             u = retrieve[p, j - 1]
-            tok = tree_tokens[retrieve[p, j]]
+            c = retrieve[p, j]
+            tok = tree_tokens[c]
             if mode == GREEDY:
                 ok = tok == amax[u]
                 srt = np.sort(logits[u])
@@ -83,7 +91,11 @@ def evaluate_posterior_one(tree, logits, tree_tokens, mode, temperature=0.0, eps
                 q, thr = stats[u]
                 prob = q[tok]
                 ok = decide_dtype(prob) > decide_dtype(thr)
-                margins.append(("typical_rel", float(abs(prob - thr) / max(thr, 1e-300))))
+                rel = float(abs(prob - thr) / max(thr, 1e-300))
+                margins.append(("typical_rel", rel))
+                node_margin[c] = rel
+            if c in flip:
+                ok = not ok
             if not ok:
                 break
             n += 1
@@ -106,7 +118,7 @@ def evaluate_posterior_one(tree, logits, tree_tokens, mode, temperature=0.0, eps
     sel = int(retrieve[best, a])
     next_root = int(amax[sel])
     return dict(best=best, accept_len=a, sel=sel, next_root=next_root, acc=acc, lik=lik,
-                argmax=amax, margins=margins)
+                argmax=amax, margins=margins, node_margin=node_margin)
 
 
 def evaluate_posterior(tree, logits, tree_tokens, mode, temperature=0.0, eps=0.09, delta=0.3):

@@ -26,7 +26,8 @@ EXPORTED = [
     "medusa_gemm_resid_rmsnorm_workspace_size", "medusa_gemm_resid_rmsnorm", "medusa_rope_split",
     "medusa_embed", "medusa_gather_rows", "medusa_argmax_rows", "medusa_topk_rows_workspace_size",
     "medusa_topk_rows",
-    "medusa_forward_workspace_size", "medusa_forward", "medusa_prefill_workspace_size", "medusa_prefill",
+    "medusa_forward_workspace_size", "medusa_forward", "medusa_forward_trace", "medusa_prefill_workspace_size",
+    "medusa_prefill",
     "medusa_step_workspace_size", "medusa_step", "medusa_step_graph_create", "medusa_graph_launch",
     "medusa_graph_destroy", "medusa_step_fused_workspace_size", "medusa_step_fused",
     "medusa_tree_from_acceptance", "medusa_head_hits",
@@ -56,6 +57,11 @@ class ModelDesc(C.Structure):
                 ("lm_head", C.c_void_p), ("layers", C.POINTER(LayerWeights)), ("rope_cos", C.c_void_p),
                 ("rope_sin", C.c_void_p), ("rope_max_pos", C.c_int), ("n_medusa", C.c_int),
                 ("medusa_w1", C.c_void_p), ("medusa_w2", C.c_void_p)]
+
+
+class TraceDesc(C.Structure):
+    _fields_ = [("x", C.c_void_p), ("xn", C.c_void_p), ("q", C.c_void_p), ("attn", C.c_void_p),
+                ("x_mid", C.c_void_p), ("act", C.c_void_p)]
 
 
 class StateDesc(C.Structure):
@@ -101,6 +107,8 @@ def _declare(lib):
         "medusa_forward_workspace_size": (_S, [C.POINTER(ModelDesc), _I, _I, _L]),
         "medusa_forward": (_I, [C.POINTER(ModelDesc), _I, _I, _P, _P, _P, _P, _L, _L, _P, _P, _P, _P, _P, _P, _P,
                                 _S, _P]),
+        "medusa_forward_trace": (_I, [C.POINTER(ModelDesc), _I, _I, _P, _P, _P, _P, _L, _L, _P, _P, _P, _P, _P, _P,
+                                      C.POINTER(TraceDesc), _P, _S, _P]),
         "medusa_prefill_workspace_size": (_S, [C.POINTER(ModelDesc), _I, _I, _L]),
         "medusa_prefill": (_I, [C.POINTER(ModelDesc), _I, _I, _P, C.POINTER(StateDesc), _P, _S, _P]),
         "medusa_step_workspace_size": (_S, [C.POINTER(ModelDesc), _P, _I, _L]),

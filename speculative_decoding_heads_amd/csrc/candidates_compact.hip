@@ -74,7 +74,7 @@ __global__ void compact_finalize_kernel(const medusa_tree_host* __restrict__ t, 
                                         const int32_t* __restrict__ best, const int32_t* __restrict__ accept_len,
                                         int32_t* __restrict__ seq_len, const int32_t* __restrict__ tree_tokens,
                                         int32_t* __restrict__ out_tokens, int max_new, int32_t* __restrict__ n_out,
-                                        int32_t* __restrict__ err_flag) {
+                                        int32_t* __restrict__ err_flag, int32_t* __restrict__ appended) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int a = accept_len[b];
@@ -82,6 +82,7 @@ __global__ void compact_finalize_kernel(const medusa_tree_host* __restrict__ t, 
   const int bi = best[b];
   bool bad = a < 0 || bi < 0 || bi >= t->P || a + 1 > t->path_len[bi] || s < 0 || (int64_t)s + a + 1 > Lmax;
   if (!bad && out_tokens) bad = n_out[b] < 0 || n_out[b] + a + 1 > max_new;
+  if (appended) appended[b] = bad ? 0 : 1;
   if (bad) {
     if (err_flag) *err_flag = 1;
     return;
@@ -158,16 +159,25 @@ __global__ void compact_stop_finalize_kernel(const medusa_tree_host* __restrict_
                                              const int32_t* __restrict__ best, const int32_t* __restrict__ accept_len,
                                              int32_t* __restrict__ seq_len, const int32_t* __restrict__ tree_tokens,
                                              int32_t* __restrict__ out_tokens, int max_new, int32_t* __restrict__ n_out,
-                                             int32_t* __restrict__ done, int stop, int32_t* __restrict__ err_flag) {
+                                             int32_t* __restrict__ done, int stop, int32_t* __restrict__ err_flag,
+                                             int32_t* __restrict__ appended) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B || done[b]) return;
+  if (b >= B) return;
+  if (done[b]) {
+    if (appended) appended[b] = 0;
+    return;
+  }
   const int a = accept_len[b], s = seq_len[b], bi = best[b], n = n_out[b];
   if (compact_bad(t, a, bi, s, n)) {
+    if (appended) appended[b] = 0;
     if (err_flag) *err_flag = 1;
     return;
   }
   bool fin;
   const int c = appended_count(t, tree_tokens, b, a, bi, s, n, max_new, Lmax, stop, fin);
+  // the next root and heads' input belong to the node after the last accepted
+  // token: kept only when every accepted token was appended
+  if (appended) appended[b] = c == a + 1 ? 1 : 0;
   for (int i = 0; i < c; ++i)
     out_tokens[(size_t)b * max_new + n + i] = tree_tokens[(size_t)b * t->T + t->retrieve[bi * MEDUSA_MAX_TREE + i]];
   n_out[b] = n + c;
@@ -193,11 +203,11 @@ extern "C" int tree_build_candidates(const medusa_tree* t, int B, int H, int K, 
   return check_launch("tree_build_candidates");
 }
 
-extern "C" int kv_compact(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax,
-                          void* Kc, void* Vc, const void* Kt, const void* Vt, const int32_t* best,
-                          const int32_t* accept_len, int32_t* seq_len, const int32_t* tree_tokens,
-                          int32_t* out_tokens, int max_new, int32_t* n_out, int32_t* err_flag,
-                          hipStream_t stream) {
+namespace medusa {
+int kv_compact_flags(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax, void* Kc,
+                     void* Vc, const void* Kt, const void* Vt, const int32_t* best, const int32_t* accept_len,
+                     int32_t* seq_len, const int32_t* tree_tokens, int32_t* out_tokens, int max_new, int32_t* n_out,
+                     int32_t* err_flag, int32_t* appended, hipStream_t stream) {
   MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "kv_compact: null tree");
   MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "kv_compact: dtype %d", dtype);
   MEDUSA_REQUIRE(n_layers >= 0 && B >= 0 && Hkv > 0 && Dh > 0 && Lmax > 0, MEDUSA_ERR_ARG, "kv_compact: bad sizes");
@@ -221,16 +231,14 @@ extern "C" int kv_compact(int dtype, const medusa_tree* t, int n_layers, int B, 
     if (rc) return rc;
   }
   hipLaunchKernelGGL(compact_finalize_kernel, dim3((B + 63) / 64), dim3(64), 0, stream, t->dev, B, Lmax, best,
-                     accept_len, seq_len, tree_tokens, out_tokens, max_new, n_out, err_flag);
+                     accept_len, seq_len, tree_tokens, out_tokens, max_new, n_out, err_flag, appended);
   return check_launch("kv_compact finalize");
 }
-
-namespace medusa {
 
 int kv_compact_stop(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax, void* Kc,
                     void* Vc, const void* Kt, const void* Vt, const int32_t* best, const int32_t* accept_len,
                     int32_t* seq_len, const int32_t* tree_tokens, int32_t* out_tokens, int max_new, int32_t* n_out,
-                    int32_t* done, int stop_token, int32_t* err_flag, hipStream_t stream) {
+                    int32_t* done, int stop_token, int32_t* err_flag, int32_t* appended, hipStream_t stream) {
   MEDUSA_REQUIRE(t && dtype_ok(dtype), MEDUSA_ERR_ARG, "kv_compact_stop: bad tree or dtype");
   MEDUSA_REQUIRE(n_layers >= 0 && B >= 0 && Hkv > 0 && Dh > 0 && Lmax > 0, MEDUSA_ERR_ARG,
                  "kv_compact_stop: bad sizes");
@@ -254,9 +262,19 @@ int kv_compact_stop(int dtype, const medusa_tree* t, int n_layers, int B, int Hk
     if (rc) return rc;
   }
   hipLaunchKernelGGL(compact_stop_finalize_kernel, dim3((B + 63) / 64), dim3(64), 0, stream, t->dev, B, Lmax, best,
-                     accept_len, seq_len, tree_tokens, out_tokens, max_new, n_out, done, stop_token, err_flag);
+                     accept_len, seq_len, tree_tokens, out_tokens, max_new, n_out, done, stop_token, err_flag,
+                     appended);
   return check_launch("kv_compact_stop finalize");
 }
 
 }  // namespace medusa
+
+extern "C" int kv_compact(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax,
+                          void* Kc, void* Vc, const void* Kt, const void* Vt, const int32_t* best,
+                          const int32_t* accept_len, int32_t* seq_len, const int32_t* tree_tokens,
+                          int32_t* out_tokens, int max_new, int32_t* n_out, int32_t* err_flag,
+                          hipStream_t stream) {
+  return kv_compact_flags(dtype, t, n_layers, B, Hkv, Dh, Lmax, Kc, Vc, Kt, Vt, best, accept_len, seq_len,
+                          tree_tokens, out_tokens, max_new, n_out, err_flag, nullptr, stream);
+}
 

@@ -89,10 +89,16 @@ int gemm_qkv_rope_bf16(int B, int T, int K, int Hq, int Hkv, int Dh, const bf16_
 // sequence's accepted tokens up to and including the first stop_token (< 0:
 // none) within its output and cache room, sets done[b] when it appends the stop
 // token or fills a room, and leaves sequences with done[b] set untouched.
+// Both compaction variants also write appended[b] (nullable): 1 when sequence b
+// appended all a_b + 1 accepted tokens this step, else 0 (overflow, stop, done).
 int kv_compact_stop(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax, void* Kc,
                     void* Vc, const void* Kt, const void* Vt, const int32_t* best, const int32_t* accept_len,
                     int32_t* seq_len, const int32_t* tree_tokens, int32_t* out_tokens, int max_new, int32_t* n_out,
-                    int32_t* done, int stop_token, int32_t* err_flag, hipStream_t stream);
+                    int32_t* done, int stop_token, int32_t* err_flag, int32_t* appended, hipStream_t stream);
+int kv_compact_flags(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, int Dh, int64_t Lmax, void* Kc,
+                     void* Vc, const void* Kt, const void* Vt, const int32_t* best, const int32_t* accept_len,
+                     int32_t* seq_len, const int32_t* tree_tokens, int32_t* out_tokens, int max_new, int32_t* n_out,
+                     int32_t* err_flag, int32_t* appended, hipStream_t stream);
 
 // Square-tile bf16 product for many rows (gemm_tile.hip): M >= GEMM_TILE_MIN_M,
 // K % 32 == 0, every epilogue but SwiGLU; W is [N, K] with K contiguous.

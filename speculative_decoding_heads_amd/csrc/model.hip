@@ -129,10 +129,11 @@ extern "C" size_t medusa_forward_workspace_size(const medusa_model* m, int B, in
   return fwd_layout(m, B, T, L_hint, nullptr, nullptr);
 }
 
-extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t* tokens, const int32_t* pos,
-                              const void* Kc, const void* Vc, int64_t Lmax, int64_t L_hint, const int32_t* seq_len,
-                              void* Kt, void* Vt, const uint64_t* anc, float* logits, void* h, void* ws,
-                              size_t ws_bytes, hipStream_t stream) {
+namespace {
+int forward_impl(const medusa_model* m, int B, int T, const int32_t* tokens, const int32_t* pos, const void* Kc,
+                 const void* Vc, int64_t Lmax, int64_t L_hint, const int32_t* seq_len, void* Kt, void* Vt,
+                 const uint64_t* anc, float* logits, void* h, const medusa_trace* tr, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
   int rc = check_model(m);
   if (rc) return rc;
   MEDUSA_REQUIRE(B >= 0 && T >= 1 && T <= MEDUSA_MAX_TREE, MEDUSA_ERR_ARG, "forward: bad B/T");
@@ -151,7 +152,17 @@ extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t
     int r_ = (x);      \
     if (r_) return r_; \
   } while (0)
+  // tracing: copy a stage's output into slot `slot` of a caller buffer (skipped when null)
+  auto trace = [&](void* dst, int slot, const void* src, size_t row_elems) -> int {
+    if (!dst) return MEDUSA_OK;
+    const size_t bytes = (size_t)M * row_elems * es;
+    MEDUSA_HIP(hipMemcpyAsync((char*)dst + slot * bytes, src, bytes, hipMemcpyDeviceToDevice, stream));
+    return MEDUSA_OK;
+  };
+  const medusa_trace none = {};
+  const medusa_trace& t = tr ? *tr : none;
   CK(medusa_embed(dt, M, d, tokens, m->embed, m->vocab, f.x, stream));
+  CK(trace(t.x, 0, f.x, d));
   // each residual projection also applies the RMSNorm that feeds the next
   // sub-layer (the last one the final norm, into h)
   CK(medusa_rmsnorm(dt, M, d, f.x, m->layers[0].attn_norm, m->norm_eps, f.xn, stream));
@@ -160,6 +171,7 @@ extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t
     const bool last = l + 1 == m->n_layers;
     char* kt = (char*)Kt + l * side_layer;
     char* vt = (char*)Vt + l * side_layer;
+    CK(trace(t.xn, l, f.xn, d));
     // bf16: the product's epilogue applies the rotary embedding and splits q/K/V
     const int fused = dt == MEDUSA_BF16
                           ? gemm_qkv_rope_bf16(B, T, d, Hq, Hkv, Dh, (const bf16_t*)f.xn, (const bf16_t*)w.wqkv, pos,
@@ -173,19 +185,43 @@ extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t
       CK(medusa_rope_split(dt, B, T, Hq, Hkv, Dh, (const float*)f.qkv, pos, m->rope_cos, m->rope_sin,
                            m->rope_max_pos, f.q, kt, vt, stream));
     }
+    CK(trace(t.q, l, f.q, (size_t)Hq * Dh));
     CK(tree_attention(dt, B, T, Hq, Hkv, Dh, f.q, Lmax ? (const char*)Kc + l * cache_layer : nullptr,
                       Lmax ? (const char*)Vc + l * cache_layer : nullptr, Lmax, L_hint, seq_len, kt, vt, anc, scale,
                       f.attn, f.aws, f.aws_bytes, stream));
+    CK(trace(t.attn, l, f.attn, (size_t)Hq * Dh));
     CK(medusa_gemm_resid_rmsnorm(dt, M, d, Hq * Dh, f.attn, Hq * Dh, w.wo, f.x, w.ffn_norm, m->norm_eps, f.xn, f.gws,
                                  f.gws_bytes, stream));
+    CK(trace(t.x_mid, l, f.x, d));
     CK(medusa_gemm(dt, M, 2 * F, d, f.xn, d, 0, w.w_gate_up, 0, f.act, F, 0, 1, MEDUSA_EPI_SWIGLU, nullptr, 0, 0,
                    f.gws, f.gws_bytes, stream));
+    CK(trace(t.act, l, f.act, F));
     CK(medusa_gemm_resid_rmsnorm(dt, M, d, F, f.act, F, w.w_down, f.x, last ? m->final_norm : m->layers[l + 1].attn_norm,
                                  m->norm_eps, last ? h : f.xn, f.gws, f.gws_bytes, stream));
+    CK(trace(t.x, l + 1, f.x, d));
   }
   CK(medusa_gemm(dt, M, m->vocab, d, h, d, 0, m->lm_head, 0, logits, m->vocab, 0, 1, MEDUSA_EPI_F32, nullptr, 0, 0,
                  f.gws, f.gws_bytes, stream));
   return MEDUSA_OK;
+}
+}  // namespace
+
+extern "C" int medusa_forward(const medusa_model* m, int B, int T, const int32_t* tokens, const int32_t* pos,
+                              const void* Kc, const void* Vc, int64_t Lmax, int64_t L_hint, const int32_t* seq_len,
+                              void* Kt, void* Vt, const uint64_t* anc, float* logits, void* h, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(m, B, T, tokens, pos, Kc, Vc, Lmax, L_hint, seq_len, Kt, Vt, anc, logits, h, nullptr, ws,
+                      ws_bytes, stream);
+}
+
+extern "C" int medusa_forward_trace(const medusa_model* m, int B, int T, const int32_t* tokens, const int32_t* pos,
+                                    const void* Kc, const void* Vc, int64_t Lmax, int64_t L_hint,
+                                    const int32_t* seq_len, void* Kt, void* Vt, const uint64_t* anc, float* logits,
+                                    void* h, const medusa_trace* trace, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  MEDUSA_REQUIRE(trace, MEDUSA_ERR_ARG, "forward_trace: null trace");
+  return forward_impl(m, B, T, tokens, pos, Kc, Vc, Lmax, L_hint, seq_len, Kt, Vt, anc, logits, h, trace, ws,
+                      ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -276,7 +312,7 @@ extern "C" int medusa_prefill(const medusa_model* m, int B, int S, const int32_t
 // ---------------------------------------------------------------------------
 namespace {
 struct StepBufs {
-  int32_t *topk, *tok, *pos, *cart, *next_root;
+  int32_t *topk, *tok, *pos, *cart, *next_root, *appended;
   void *Kt, *Vt, *h;
   float* logits;
   void *hws, *fws, *pws;
@@ -292,6 +328,7 @@ size_t step_layout(const medusa_model* m, const medusa_tree* t, int B, int64_t L
   s.pos = (int32_t*)c.take((size_t)B * T * 4);
   s.cart = (int32_t*)c.take((size_t)B * P * (D + 1) * 4);
   s.next_root = (int32_t*)c.take((size_t)B * 4);
+  s.appended = (int32_t*)c.take((size_t)B * 4);
   const size_t side = (size_t)m->n_layers * B * m->n_kv_heads * T * m->head_dim * es;
   s.Kt = c.take(side);
   s.Vt = c.take(side);
@@ -310,16 +347,44 @@ size_t step_layout(const medusa_model* m, const medusa_tree* t, int B, int64_t L
 
 namespace {
 // KV compaction and token append of a step, with per-sequence stop when the
-// state carries done flags
+// state carries done flags; appended[b] says whether sequence b took all its
+// accepted tokens
 int compact_state(const medusa_model* m, const medusa_tree* t, int B, medusa_state* st, const void* Kt,
-                  const void* Vt, const int32_t* tok, hipStream_t stream) {
+                  const void* Vt, const int32_t* tok, int32_t* appended, hipStream_t stream) {
   if (st->done)
     return kv_compact_stop(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, Kt, Vt,
                            st->best, st->accept_len, st->seq_len, tok, st->out_tokens, st->max_new, st->n_out,
-                           st->done, st->stop_token, st->err, stream);
-  return kv_compact(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, Kt, Vt,
-                    st->best, st->accept_len, st->seq_len, tok, st->out_tokens, st->max_new, st->n_out, st->err,
-                    stream);
+                           st->done, st->stop_token, st->err, appended, stream);
+  return kv_compact_flags(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, Kt, Vt,
+                          st->best, st->accept_len, st->seq_len, tok, st->out_tokens, st->max_new, st->n_out, st->err,
+                          appended, stream);
+}
+
+// The next step's inputs, for the sequences that appended this step's tokens:
+// root[b] = next_root[b] and h_sel[b] = h[b, sel[b]] (section 二.7: the next
+// candidates come from the position the accepted path ends at).  A sequence
+// that appended nothing (cache or output full, finished) keeps both, so its
+// state still matches its cache.
+template <typename TY>
+__global__ void commit_step_kernel(int T, int d, const TY* __restrict__ h, const int32_t* __restrict__ sel,
+                                   const int32_t* __restrict__ appended, const int32_t* __restrict__ next_root,
+                                   int32_t* __restrict__ root, TY* __restrict__ h_sel) {
+  const int b = blockIdx.x;
+  if (!appended[b]) return;
+  int s = sel[b];
+  s = s < 0 ? 0 : (s >= T ? T - 1 : s);
+  for (int n = threadIdx.x; n < d; n += blockDim.x) h_sel[(size_t)b * d + n] = h[((size_t)b * T + s) * d + n];
+  if (threadIdx.x == 0) root[b] = next_root[b];
+}
+
+int commit_step(const medusa_model* m, int B, int T, const StepBufs& s, medusa_state* st, hipStream_t stream) {
+  if (m->dtype == MEDUSA_BF16)
+    hipLaunchKernelGGL(commit_step_kernel<bf16_t>, dim3(B), dim3(256), 0, stream, T, m->d, (const bf16_t*)s.h,
+                       st->sel_node, s.appended, s.next_root, st->root, (bf16_t*)st->h_sel);
+  else
+    hipLaunchKernelGGL(commit_step_kernel<float>, dim3(B), dim3(256), 0, stream, T, m->d, (const float*)s.h,
+                       st->sel_node, s.appended, s.next_root, st->root, (float*)st->h_sel);
+  return check_launch("step commit");
 }
 }  // namespace
 
@@ -353,9 +418,9 @@ extern "C" int medusa_step(const medusa_model* m, const medusa_tree* t, int B, i
   CK(medusa_forward(m, B, T, s.tok, s.pos, st->Kc, st->Vc, st->Lmax, L_hint, st->seq_len, s.Kt, s.Vt, t->dev->anc,
                     s.logits, s.h, s.fws, s.fws_bytes, stream));
   CK(evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best, st->accept_len,
-                        st->sel_node, st->root, s.pws, s.pws_bytes, stream));
-  CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, stream));
-  CK(medusa_gather_rows(m->dtype, B, T, m->d, s.h, st->sel_node, st->h_sel, stream));
+                        st->sel_node, s.next_root, s.pws, s.pws_bytes, stream));
+  CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, s.appended, stream));
+  CK(commit_step(m, B, T, s, st, stream));
   return MEDUSA_OK;
 #undef CK
 }
@@ -366,10 +431,12 @@ extern "C" int medusa_step(const medusa_model* m, const medusa_tree* t, int B, i
 namespace {
 
 // carry[b] = all[b * T + sel[b]]: the H*K top-K entries of the node each
-// sequence's accepted path ends at (sel clamped to [0, T))
+// sequence's accepted path ends at (sel clamped to [0, T)); kept unchanged for
+// a sequence that appended nothing this step
 __global__ void gather_topk_kernel(int T, int HK, const int32_t* __restrict__ all, const int32_t* __restrict__ sel,
-                                   int32_t* __restrict__ carry) {
+                                   const int32_t* __restrict__ appended, int32_t* __restrict__ carry) {
   const int b = blockIdx.x;
+  if (!appended[b]) return;
   int s = sel[b];
   s = s < 0 ? 0 : (s >= T ? T - 1 : s);
   for (int i = threadIdx.x; i < HK; i += blockDim.x) carry[(size_t)b * HK + i] = all[((size_t)b * T + s) * HK + i];
@@ -434,11 +501,11 @@ extern "C" int medusa_step_fused(const medusa_model* m, const medusa_tree* t, in
   CK(medusa_heads_topk(m->dtype, B * T, m->d, m->vocab, H, K, s.h, m->medusa_w1, m->medusa_w2, f.topk_all, nullptr,
                        f.hws, f.hws_bytes, stream));
   CK(evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best, st->accept_len,
-                        st->sel_node, st->root, s.pws, s.pws_bytes, stream));
-  CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, stream));
-  CK(medusa_gather_rows(m->dtype, B, T, m->d, s.h, st->sel_node, st->h_sel, stream));
+                        st->sel_node, s.next_root, s.pws, s.pws_bytes, stream));
+  CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, s.appended, stream));
+  CK(commit_step(m, B, T, s, st, stream));
   hipLaunchKernelGGL(gather_topk_kernel, dim3(B), dim3(64), 0, stream, T, H * K, f.topk_all, st->sel_node,
-                     topk_carry);
+                     s.appended, topk_carry);
   return check_launch("step_fused carry");
 #undef CK
 }

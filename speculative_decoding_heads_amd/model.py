@@ -74,8 +74,19 @@ class Model:
     def forward_workspace_size(self, B, T, L_hint):
         return lib().medusa_forward_workspace_size(C.byref(self.desc), B, T, int(L_hint))
 
-    def forward(self, tokens, pos, Kc, Vc, seq_len, anc, L_hint=None, Kt=None, Vt=None, ws=None):
-        """tokens, pos [B, T] int32; Kc/Vc [NL, B, Hkv, Lmax, Dh] -> (logits [B,T,V], h [B,T,d], Kt, Vt)."""
+    def trace_buffers(self, B, T):
+        """Device buffers for forward(..., trace=...): each stage's output of every layer."""
+        torch = _torch()
+        M, dev, dt = B * T, self.device, self.dtype
+        e = lambda *s: torch.empty(s, dtype=dt, device=dev)
+        return dict(x=e(self.NL + 1, M, self.d), xn=e(self.NL, M, self.d), q=e(self.NL, M, self.Hq * self.Dh),
+                    attn=e(self.NL, M, self.Hq * self.Dh), x_mid=e(self.NL, M, self.d), act=e(self.NL, M, self.F))
+
+    def forward(self, tokens, pos, Kc, Vc, seq_len, anc, L_hint=None, Kt=None, Vt=None, ws=None, trace=None):
+        """tokens, pos [B, T] int32; Kc/Vc [NL, B, Hkv, Lmax, Dh] -> (logits [B,T,V], h [B,T,d], Kt, Vt).
+
+        trace: optional dict of device buffers (trace_buffers(B, T)) that receive each
+        stage's output of every layer (medusa_forward_trace)."""
         torch = _torch()
         B, T = tokens.shape
         Lmax = Kc.shape[3] if Kc is not None else 0
@@ -88,9 +99,21 @@ class Model:
         h = torch.empty((B, T, self.d), dtype=self.dtype, device=dev)
         ws = L._ws(ws, self.forward_workspace_size(B, T, L_hint), dev)
         anc_p = anc.anc_device if hasattr(anc, "anc_device") else ptr(anc)
-        check(lib().medusa_forward(C.byref(self.desc), B, T, ptr(tokens), ptr(pos), ptr(Kc), ptr(Vc), Lmax, L_hint,
-                                   ptr(seq_len), ptr(Kt), ptr(Vt), anc_p, ptr(logits), ptr(h), ptr(ws), ws.numel(),
-                                   stream_ptr()))
+        if trace is not None:
+            M = B * T
+            shapes = dict(x=(self.NL + 1, M, self.d), xn=(self.NL, M, self.d), q=(self.NL, M, self.Hq * self.Dh),
+                          attn=(self.NL, M, self.Hq * self.Dh), x_mid=(self.NL, M, self.d), act=(self.NL, M, self.F))
+            for k, v in trace.items():
+                if k not in shapes or tuple(v.shape) != shapes[k] or v.dtype != self.dtype:
+                    raise MedusaError("forward: trace buffer %s must be %s %s" % (k, shapes.get(k), self.dtype))
+            td = L.TraceDesc(*[ptr(trace.get(k)) for k in ("x", "xn", "q", "attn", "x_mid", "act")])
+            check(lib().medusa_forward_trace(C.byref(self.desc), B, T, ptr(tokens), ptr(pos), ptr(Kc), ptr(Vc), Lmax,
+                                             L_hint, ptr(seq_len), ptr(Kt), ptr(Vt), anc_p, ptr(logits), ptr(h),
+                                             C.byref(td), ptr(ws), ws.numel(), stream_ptr()))
+        else:
+            check(lib().medusa_forward(C.byref(self.desc), B, T, ptr(tokens), ptr(pos), ptr(Kc), ptr(Vc), Lmax,
+                                       L_hint, ptr(seq_len), ptr(Kt), ptr(Vt), anc_p, ptr(logits), ptr(h), ptr(ws),
+                                       ws.numel(), stream_ptr()))
         return logits, h, Kt, Vt
 
 

@@ -16,7 +16,7 @@ from oracle.posterior import GREEDY, TYPICAL, evaluate_posterior_one
 from oracle.tree import tree_buffers
 from workloads import PAGE_TREE_CHOICES, TWO_HEAD_CHOICES, TinyConfig, prompt_tokens, seeded_tree_choices, tiny_model
 
-from _gpu import assert_close, say, to_dev, to_np
+from _gpu import assert_close, layer_stage_parity, posterior_outcome, say, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -209,6 +209,45 @@ def test_tiny_fp32_state_after_steps(dev):
     assert_close(to_np(st.Vc)[:, 0, :, :S], cV[:, 0, :, :S], rtol=1e-5, atol=1e-5, what="V cache")
 
 
+BF16_TOL = dict(rtol=2e-2, atol=1e-2)
+# Unconditional comparison (the oracle's own residual stream from the tokens): bf16
+# rounding of every stored activation happens on each side separately, and a small
+# difference entering a stage is carried -- and, through each RMSNorm of a small
+# residual stream, enlarged -- through the rest of the stack.  Measured logits bound
+# for these models (absolute); every stage given the GPU's own input holds the stated
+# 2e-2 relative / 1e-2 absolute.
+E2E_LOGIT_ATOL = 5e-2
+
+
+def _forward_parity(dev, model, params, tok, pos, gKc, gVc, seq, tree, ot, Lmax, Kc, Vc):
+    """bf16 forward against the oracle: every stage of every layer on the GPU's own
+    input to it (conditional, stated tolerance), the final norm and LM head on the
+    GPU's last stream, and the whole stack from the tokens (unconditional, measured
+    bound)."""
+    import torch
+    from oracle.decoder import embed_tokens, final_logits
+    NL, B, T = len(params["layers"]), tok.shape[0], tok.shape[1]
+    trace = model.trace_buffers(B, T)
+    logits, h, Kt, Vt = model.forward(tok, pos, gKc, gVc, seq, tree, L_hint=Lmax, trace=trace)
+    torch.cuda.synchronize()
+    tr = {k: to_np(v).astype(np.float64) for k, v in trace.items()}
+    toks, pos_np, seq_np = to_np(tok), to_np(pos), to_np(seq)
+    assert_close(tr["x"][0].reshape(B, T, -1), embed_tokens(params, toks, bf16=True), rtol=0, atol=0,
+                 what="embedding rows")
+    gK, gV = to_np(Kt), to_np(Vt)
+    for l in range(NL):
+        layer_stage_parity(params, params["layers"][l], l, tr, Kc[l], Vc[l], gK[l], gV[l], pos_np, seq_np, ot["anc"])
+    rl, rh = final_logits(params, tr["x"][NL].reshape(B, T, -1), bf16=True)
+    gl = to_np(logits)
+    assert_close(to_np(h), rh, what="h", **BF16_TOL)
+    assert_close(gl, rl, what="logits", **BF16_TOL)
+    own, _, _, _ = oracle_forward(params, toks, pos_np, Kc, Vc, seq_np, ot["anc"], bf16=True)
+    e2e = float(np.abs(gl - own).max())
+    print("[forward] unconditional logits max |diff| %.3g (max |logit| %.3g)" % (e2e, float(np.abs(own).max())),
+          flush=True)
+    assert e2e <= E2E_LOGIT_ATOL, e2e
+
+
 def _small_bf16_model(seed, heads_kv_dim=(8, 4, 64)):
     class Cfg:
         n_layers = 2
@@ -253,15 +292,8 @@ def test_bf16_forward_vs_oracle(dev, heads_kv_dim, B, tree_name):
     toks = rng.integers(0, Cfg.vocab, (B, ot["T"])).astype(np.int32)
     pos = (seq[:, None] + ot["depth"][None, :]).astype(np.int32)
     d = lambda x: torch.from_numpy(x).to(dev)
-    logits, h, Kt, Vt = model.forward(d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev), to_dev(Vc, torch.bfloat16, dev),
-                                      d(seq), tree, L_hint=Lmax)
-    torch.cuda.synchronize()
-    rl, rh, rK, rV = oracle_forward(params, toks, pos, Kc, Vc, seq, ot["anc"], bf16=True)
-    scale = np.abs(rl).max()
-    assert_close(to_np(logits), rl, rtol=2e-2, atol=1e-2 * max(scale, 1.0), what="logits")
-    assert_close(to_np(h), rh, rtol=2e-2, atol=1e-2 * np.abs(rh).max(), what="h")
-    assert_close(to_np(Kt), rK, rtol=2e-2, atol=1e-2 * np.abs(rK).max(), what="tree K")
-    assert_close(to_np(Vt), rV, rtol=2e-2, atol=1e-2 * np.abs(rV).max(), what="tree V")
+    _forward_parity(dev, model, params, d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev),
+                    to_dev(Vc, torch.bfloat16, dev), d(seq), tree, ot, Lmax, Kc, Vc)
 
 
 def test_bf16_forward_full_width_layer(dev):
@@ -298,14 +330,8 @@ def test_bf16_forward_full_width_layer(dev):
     toks = rng.integers(0, Cfg.vocab, (B, 64)).astype(np.int32)
     pos = (seq[:, None] + ot["depth"][None, :]).astype(np.int32)
     d = lambda x: torch.from_numpy(x).to(dev)
-    logits, h, Kt, Vt = model.forward(d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev), to_dev(Vc, torch.bfloat16, dev),
-                                      d(seq), tree, L_hint=Lmax)
-    torch.cuda.synchronize()
-    rl, rh, rK, rV = oracle_forward(params, toks, pos, Kc, Vc, seq, ot["anc"], bf16=True)
-    assert_close(to_np(Kt), rK, rtol=2e-2, atol=1e-2 * np.abs(rK).max(), what="tree K")
-    assert_close(to_np(Vt), rV, rtol=2e-2, atol=1e-2 * np.abs(rV).max(), what="tree V")
-    assert_close(to_np(h), rh, rtol=2e-2, atol=1e-2 * np.abs(rh).max(), what="h")
-    assert_close(to_np(logits), rl, rtol=2e-2, atol=1e-2 * max(np.abs(rl).max(), 1.0), what="logits")
+    _forward_parity(dev, model, params, d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev),
+                    to_dev(Vc, torch.bfloat16, dev), d(seq), tree, ot, Lmax, Kc, Vc)
 
 
 @pytest.mark.parametrize("mode", [GREEDY, TYPICAL])
@@ -337,12 +363,10 @@ def test_bf16_step_acceptance_on_identical_logits(dev, mode):
     logits, h, Kt, Vt = model.forward(tok, pos, Kc0, Vc0, seq0, tree, L_hint=Lmax)
     torch.cuda.synchronize()
     lg, tk = to_np(logits), to_np(tok)
+    near = 0
     for b in range(B):
-        r = evaluate_posterior_one(ot, lg[b], tk[b], mode, tau, 0.09, 0.3)
         got = tuple(int(to_np(x)[b]) for x in (st.best, st.accept_len, st.sel_node, st.root))
-        ref = (r["best"], r["accept_len"], r["sel"], r["next_root"])
-        if got != ref:
-            assert any(k != "argmax_gap" and m < 1e-5 for k, m in r["margins"]), (b, got, ref)
+        near += posterior_outcome(ot, lg[b], tk[b], mode, tau, 0.09, 0.3, got)
         # compaction: cache rows seq0..seq0+a hold the chosen path's K/V
         a, bi = int(to_np(st.accept_len)[b]), int(to_np(st.best)[b])
         s0 = int(to_np(seq0)[b])
@@ -351,6 +375,7 @@ def test_bf16_step_acceptance_on_identical_logits(dev, mode):
         assert torch.equal(st.Vc[:, b, :, s0:s0 + a + 1], Vt[:, b][:, :, rows])
         assert int(to_np(st.seq_len)[b]) == s0 + a + 1
         assert torch.equal(st.h_sel[b], h[b, int(to_np(st.sel_node)[b])])
+    assert near <= 1
 
 
 def test_bf16_fused_step_carry_and_state(dev):

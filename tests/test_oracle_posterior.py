@@ -1,12 +1,11 @@
 """Pins of the oracle's acceptance rule (CPU): hand-built greedy cases, closed-form
 typical thresholds on uniform / two-point distributions, the eps/temperature
-special cases, the padding reading, and a cross-check against a per-path tensor
-formulation in the style of the page's code."""
+special cases, the padding reading, and a cross-check against a node-by-node
+reachability formulation of the same rule."""
 import math
 
 import numpy as np
 import pytest
-import torch
 
 from oracle.posterior import GREEDY, TYPICAL, evaluate_posterior, evaluate_posterior_one
 from oracle.tree import tree_buffers
@@ -133,39 +132,53 @@ def test_small_temperature_equals_greedy():
         assert ty["sel"] == g["sel"]  # greedy's accepted prefix is unique
 
 
-def _page_style(tree, logits, toks, mode, tau=0.7, eps=0.09, delta=0.3):
-    """Per-path tensor formulation: gather path logits by retrieve, cumulative product of
-    per-position accept flags, then max / first-argmax / likelihood (pads masked out)."""
-    lg = torch.from_numpy(np.asarray(logits, np.float64))
-    ret = torch.from_numpy(tree["retrieve"])
-    valid = ret >= 0
-    ext = torch.cat([torch.from_numpy(toks), torch.zeros(1, dtype=torch.long)])
-    cart = ext[ret]
-    plog = lg[ret.clamp(min=0)]  # [P, D+1, V]
-    if mode == GREEDY:
-        mask = (cart[:, 1:] == plog[:, :-1].argmax(-1)) & valid[:, 1:]
-    else:
-        prob = torch.softmax(plog[:, :-1] / tau, dim=-1)
-        cprob = prob.gather(-1, cart[:, 1:].unsqueeze(-1)).squeeze(-1)
-        ent = -(prob * torch.log(prob + 1e-5)).sum(-1)
-        thr = torch.minimum(torch.full_like(ent, eps), torch.exp(-ent) * delta)
-        mask = (cprob.float() > thr.float()) & valid[:, 1:]
-    acc = torch.cumprod(mask.int(), dim=1).sum(1)
-    a = int(acc.max())
+def _reachability_form(tree, logits, toks, mode, tau=0.7, eps=0.09, delta=0.3):
+    """The acceptance rule restated node by node (an independent formulation of
+    section 二.6 / 一.3, not a per-path computation): a node is reached when its
+    parent is reached and its own candidate passes the test taken at the parent;
+    the accepted length is the depth of the deepest reached node; the chosen path
+    is one whose entry at that depth is a deepest reached node -- the first such
+    path for greedy, for typical the one whose node has the largest summed log q
+    along its chain (first on equal sums).  q comes from a log-sum-exp log-softmax
+    and the entropy from those log-probabilities."""
+    T, parent, depth = tree["T"], tree["parent"], tree["depth"]
+    lg = np.asarray(logits, np.float64)
+    if mode == TYPICAL:
+        z = lg / tau
+        zmax = z.max(axis=1, keepdims=True)
+        logq = z - (zmax + np.log(np.exp(z - zmax).sum(axis=1, keepdims=True)))
+        q = np.exp(logq)
+        ent = -(q * np.log(q + 1e-5)).sum(axis=1)
+        thr = np.minimum(eps, delta * np.exp(-ent))
+    reached = np.zeros(T, bool)
+    reached[0] = True
+    chain = np.zeros(T)
+    for c in range(1, T):  # nodes are numbered depth by depth: parent[c] < c
+        u = parent[c]
+        if not reached[u]:
+            continue
+        if mode == GREEDY:
+            ok = toks[c] == int(np.argmax(lg[u]))
+        else:
+            ok = np.float32(q[u, toks[c]]) > np.float32(thr[u])
+        if ok:
+            reached[c] = True
+            chain[c] = chain[u] + (logq[u, toks[c]] if mode == TYPICAL else 0.0)
+    a = int(depth[reached].max())
+    ret, plen = tree["retrieve"], tree["path_len"]
+    ends = [p for p in range(tree["P"]) if plen[p] > a and reached[ret[p, a]]]
     if a == 0:
         best = 0
     elif mode == GREEDY:
-        best = int(torch.argmax(acc))
+        best = ends[0]
     else:
-        cands = torch.where(acc == a)[0]
-        lik = torch.log(cprob[cands, :a]).sum(-1)
-        best = int(cands[torch.argmax(lik)])
+        best = max(ends, key=lambda p: (chain[ret[p, a]], -p))
     sel = int(ret[best, a])
-    return best, a, sel, int(lg[sel].argmax())
+    return best, a, sel, int(np.argmax(lg[sel]))
 
 
 @pytest.mark.parametrize("mode", [GREEDY, TYPICAL])
-def test_cross_check_against_per_path_tensor_form(mode):
+def test_cross_check_against_node_reachability_form(mode):
     rng = np.random.default_rng(21 + mode)
     for choices in (PAGE_TREE_CHOICES, seeded_tree_choices(0), TWO_HEAD_CHOICES):
         t = tree_buffers(choices)
@@ -179,8 +192,21 @@ def test_cross_check_against_per_path_tensor_form(mode):
                 if rng.uniform() < 0.7:
                     toks[c] = amax[t["parent"][c]]
             r = evaluate_posterior_one(t, lg, toks, mode, 0.7, 0.09, 0.3)
-            ref = _page_style(t, lg, toks, mode)
+            ref = _reachability_form(t, lg, toks, mode)
             assert (r["best"], r["accept_len"], r["sel"], r["next_root"]) == ref
+
+
+def test_flip_hook_inverts_one_decision():
+    """Inverting the decision on one node changes the outcome exactly as the rule says:
+    rejecting a reached node's candidate ends that chain there."""
+    t = tree_buffers(TWO_HEAD_CHOICES)
+    toks = np.array([0, 10, 11, 20, 21, 22, 30, 31, 32])
+    amax = [11, 0, 31, 0, 0, 0, 0, 9, 0]
+    lg = _onehot_logits(9, 40, amax)
+    r = evaluate_posterior_one(t, lg, toks, GREEDY, flip={7})
+    assert (r["best"], r["accept_len"], r["sel"], r["next_root"]) == (0, 1, 2, 31)
+    r = evaluate_posterior_one(t, lg, toks, GREEDY, flip={1})  # node 1 (token 10) now accepted at the root
+    assert r["acc"].tolist() == [1, 2, 1, 1, 1, 1] and r["best"] == 1
 
 
 def test_batch_wrapper():
