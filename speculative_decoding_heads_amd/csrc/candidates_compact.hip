@@ -190,8 +190,8 @@ __global__ void compact_stop_finalize_kernel(const medusa_tree_host* __restrict_
 extern "C" int tree_build_candidates(const medusa_tree* t, int B, int H, int K, const int32_t* root,
                                      const int32_t* topk_idx, const int32_t* seq_len, int32_t* tree_tokens,
                                      int32_t* tree_pos, int32_t* cart, hipStream_t stream) {
-  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "tree_build_candidates: null tree");
   MEDUSA_REQUIRE(B >= 0, MEDUSA_ERR_ARG, "tree_build_candidates: B < 0");
+  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "tree_build_candidates: null tree");
   MEDUSA_REQUIRE(H >= t->host.D, MEDUSA_ERR_ARG, "tree_build_candidates: H=%d < tree depth %d", H, t->host.D);
   MEDUSA_REQUIRE(K == t->host.K, MEDUSA_ERR_ARG, "tree_build_candidates: K=%d but the tree uses %d", K,
                  t->host.K);
@@ -208,12 +208,12 @@ int kv_compact_flags(int dtype, const medusa_tree* t, int n_layers, int B, int H
                      void* Vc, const void* Kt, const void* Vt, const int32_t* best, const int32_t* accept_len,
                      int32_t* seq_len, const int32_t* tree_tokens, int32_t* out_tokens, int max_new, int32_t* n_out,
                      int32_t* err_flag, int32_t* appended, hipStream_t stream) {
-  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "kv_compact: null tree");
   MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "kv_compact: dtype %d", dtype);
   MEDUSA_REQUIRE(n_layers >= 0 && B >= 0 && Hkv > 0 && Dh > 0 && Lmax > 0, MEDUSA_ERR_ARG, "kv_compact: bad sizes");
   MEDUSA_REQUIRE(((size_t)Dh * dtype_size(dtype)) % 16 == 0, MEDUSA_ERR_UNSUPPORTED,
                  "kv_compact: a K/V row must be a multiple of 16 bytes");
   MEDUSA_REQUIRE(!out_tokens || (n_out && max_new > 0), MEDUSA_ERR_ARG, "kv_compact: out_tokens needs n_out");
+  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "kv_compact: null tree");
   if (B == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(best && accept_len && seq_len && tree_tokens, MEDUSA_ERR_ARG, "kv_compact: null pointer");
   if (n_layers > 0) {

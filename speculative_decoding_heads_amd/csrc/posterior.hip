@@ -210,12 +210,12 @@ extern "C" int evaluate_posterior(const medusa_tree* t, int B, int V, const floa
                                   int mode, float temperature, float eps, float delta, int32_t* best,
                                   int32_t* accept_len, int32_t* sel_node, int32_t* next_root, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
-  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "evaluate_posterior: null tree");
   MEDUSA_REQUIRE(B >= 0 && V > 0, MEDUSA_ERR_ARG, "evaluate_posterior: bad sizes");
   MEDUSA_REQUIRE(mode == MEDUSA_GREEDY || mode == MEDUSA_TYPICAL, MEDUSA_ERR_ARG, "evaluate_posterior: mode %d",
                  mode);
   MEDUSA_REQUIRE(mode == MEDUSA_GREEDY || temperature > 0.f, MEDUSA_ERR_ARG,
                  "evaluate_posterior: typical acceptance needs temperature > 0");
+  MEDUSA_REQUIRE(t, MEDUSA_ERR_ARG, "evaluate_posterior: null tree");
   MEDUSA_REQUIRE(t->host.P <= 64, MEDUSA_ERR_UNSUPPORTED, "evaluate_posterior: more than 64 paths");
   if (B == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(logits && tree_tokens && best && accept_len && sel_node && next_root, MEDUSA_ERR_ARG,
