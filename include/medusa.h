@@ -158,6 +158,23 @@ int tree_attention(int dtype, int B, int T, int Hq, int Hkv, int Dh, const void*
                    hipStream_t stream);
 
 /*
+ * tree_attention without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, serving loops that forbid
+ * allocation).  Same arguments, kernels and results as tree_attention; the split
+ * partials go to a fixed array inside the library (tree_attention_noalloc_max_scratch()
+ * bytes, 64 MiB, held on every device the library runs on until the process
+ * ends).  A shape whose tree_attention_workspace_size exceeds that returns
+ * MEDUSA_ERR_WORKSPACE before anything is launched.  Nothing in the array needs
+ * clearing between calls; every call on one device shares it, so calls that
+ * overlap on one device (different streams, or graphs replayed concurrently)
+ * race and must be serialised by the caller.
+ */
+size_t tree_attention_noalloc_max_scratch(void);
+int tree_attention_noalloc(int dtype, int B, int T, int Hq, int Hkv, int Dh, const void* q, const void* Kc,
+                           const void* Vc, int64_t Lmax, int64_t L_hint, const int32_t* seq_len, const void* Kt,
+                           const void* Vt, const uint64_t* anc, float scale, void* out, hipStream_t stream);
+
+/*
  * Acceptance (section 二.6 evaluate_posterior, section 一.3 typical acceptance):
  *   GREEDY : candidate accepted iff it equals argmax of its parent's logits.
  *   TYPICAL: q = softmax(logits/temperature) at the parent, H = -sum q log(q+1e-5),

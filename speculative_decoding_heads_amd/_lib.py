@@ -21,7 +21,8 @@ EXPORTED = [
     "medusa_last_error", "medusa_version", "medusa_tree_create", "medusa_tree_build_host", "medusa_tree_info",
     "medusa_tree_anc_device",
     "medusa_tree_destroy", "medusa_heads_topk_workspace_size", "medusa_heads_topk", "tree_build_candidates",
-    "tree_attention_workspace_size", "tree_attention", "evaluate_posterior_workspace_size", "evaluate_posterior",
+    "tree_attention_workspace_size", "tree_attention", "tree_attention_noalloc_max_scratch", "tree_attention_noalloc",
+    "evaluate_posterior_workspace_size", "evaluate_posterior",
     "kv_compact", "medusa_gemm_workspace_size", "medusa_gemm", "medusa_rmsnorm",
     "medusa_gemm_resid_rmsnorm_workspace_size", "medusa_gemm_resid_rmsnorm", "medusa_rope_split",
     "medusa_embed", "medusa_gather_rows", "medusa_argmax_rows", "medusa_topk_rows_workspace_size",
@@ -90,6 +91,8 @@ def _declare(lib):
         "tree_build_candidates": (_I, [_P, _I, _I, _I] + [_P] * 6 + [_P]),
         "tree_attention_workspace_size": (_S, [_I] * 6 + [_L]),
         "tree_attention": (_I, [_I] * 6 + [_P, _P, _P, _L, _L, _P, _P, _P, _P, _F, _P, _P, _S, _P]),
+        "tree_attention_noalloc_max_scratch": (_S, []),
+        "tree_attention_noalloc": (_I, [_I] * 6 + [_P, _P, _P, _L, _L, _P, _P, _P, _P, _F, _P, _P]),
         "evaluate_posterior_workspace_size": (_S, [_I, _I]),
         "evaluate_posterior": (_I, [_P, _I, _I, _P, _P, _I, _F, _F, _F, _P, _P, _P, _P, _P, _S, _P]),
         "kv_compact": (_I, [_I, _P, _I, _I, _I, _I, _L] + [_P] * 9 + [_I, _P, _P, _P]),

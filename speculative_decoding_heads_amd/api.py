@@ -125,6 +125,24 @@ def tree_attention(q, Kc, Vc, seq_len, Kt, Vt, anc, scale, L_hint=None, out=None
     return out
 
 
+def tree_attention_noalloc(q, Kc, Vc, seq_len, Kt, Vt, anc, scale, L_hint=None, out=None):
+    """tree_attention with the split partials in the library's fixed scratch (no workspace)."""
+    torch = _torch()
+    B, T, Hq, Dh = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    if Kc.shape != (B, Hkv, Lmax, Dh) or Vc.shape != Kc.shape or Kt.shape != (B, Hkv, T, Dh) or Vt.shape != Kt.shape:
+        raise MedusaError("tree_attention_noalloc: shape mismatch")
+    if seq_len.dtype != torch.int32:
+        raise MedusaError("tree_attention_noalloc: seq_len must be int32")
+    L_hint = Lmax if L_hint is None else int(L_hint)
+    if out is None:
+        out = torch.empty_like(q)
+    anc_p = anc.anc_device if isinstance(anc, Tree) else ptr(anc)
+    check(lib().tree_attention_noalloc(dtype_code(q), B, T, Hq, Hkv, Dh, ptr(q), ptr(Kc), ptr(Vc), Lmax, L_hint,
+                                       ptr(seq_len), ptr(Kt), ptr(Vt), anc_p, float(scale), ptr(out), stream_ptr()))
+    return out
+
+
 def evaluate_posterior(tree, logits, tree_tokens, mode, temperature=0.0, eps=0.09, delta=0.3, outs=None, ws=None):
     """logits [B,T,V] fp32, tree_tokens [B,T] int32 -> (best, accept_len, sel_node, next_root) int32 [B]."""
     torch = _torch()

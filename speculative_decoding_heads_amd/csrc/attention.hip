@@ -22,6 +22,8 @@
 //    attn_combine (below) merges.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "attn_stream.h"
 #include "common.h"
 
@@ -310,4 +312,57 @@ extern "C" int tree_attention(int dtype, int B, int T, int Hq, int Hkv, int Dh, 
   }
 #undef GEN_LAUNCH
   return check_launch("tree_attention generic");
+}
+
+// ---------------------------------------------------------------------------
+// tree_attention for callers that cannot allocate: the split partials live in
+// a fixed device array of the library instead of a caller workspace
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of this device's copy of `scratch`, looked up once per
+// device with that device current (the array's name is only a host-side
+// stand-in: never pass it to a kernel or a copy).
+int scratch_address(void** out) {
+  int dev = -1;
+  MEDUSA_HIP(hipGetDevice(&dev));
+  MEDUSA_REQUIRE(dev >= 0 && dev < kMaxDevices, MEDUSA_ERR_UNSUPPORTED, "tree_attention_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    MEDUSA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    MEDUSA_REQUIRE(p != nullptr, MEDUSA_ERR_HIP, "tree_attention_noalloc: no address for the scratch array");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t tree_attention_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+extern "C" int tree_attention_noalloc(int dtype, int B, int T, int Hq, int Hkv, int Dh, const void* q, const void* Kc,
+                                      const void* Vc, int64_t Lmax, int64_t L_hint, const int32_t* seq_len,
+                                      const void* Kt, const void* Vt, const uint64_t* anc, float scale, void* out,
+                                      hipStream_t stream) {
+  const size_t need = tree_attention_workspace_size(dtype, B, T, Hq, Hkv, Dh, L_hint);
+  MEDUSA_REQUIRE(need <= kNoAllocScratchBytes, MEDUSA_ERR_WORKSPACE,
+                 "tree_attention_noalloc: this shape needs %zu bytes of split partials, more than the %zu-byte "
+                 "static scratch; use tree_attention with a workspace",
+                 need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_address(&ws);
+    if (rc) return rc;
+  }
+  return tree_attention(dtype, B, T, Hq, Hkv, Dh, q, Kc, Vc, Lmax, L_hint, seq_len, Kt, Vt, anc, scale, out, ws,
+                        need, stream);
 }

@@ -1,4 +1,5 @@
-"""Argument errors of the five verify-step calls: each returns its documented status -- MEDUSA_ERR_ARG (-1), _UNSUPPORTED (-2)
+"""Argument errors of the five verify-step calls (and the no-allocation attention
+entry): each returns its documented status -- MEDUSA_ERR_ARG (-1), _UNSUPPORTED (-2)
 or _WORKSPACE (-3) -- with a message naming the problem, and returns before any
 device work, so these run on a machine without a GPU.  The checks that need a
 built tree (rank stride, tree depth) are in the GPU suite."""
@@ -65,6 +66,18 @@ def test_tree_attention_errors():
     _expect(_attn(ws_bytes=need - 1), WS, ["workspace"])
     _expect(_attn(ws=None, ws_bytes=need), WS, ["workspace"])
     _expect(_attn(dtype=0, Dh=256, ws=None, ws_bytes=0), UNSUP, ["Dh <= 128"])
+
+
+def test_tree_attention_noalloc_rejects_beyond_its_scratch():
+    lib = _lib()
+    cap = lib.tree_attention_noalloc_max_scratch()
+    assert cap == 64 << 20
+    # batch 51, 20/5 heads, prefix 65536: 64.7 MiB of split partials
+    need = lib.tree_attention_workspace_size(1, 51, 64, 20, 5, 128, 65536)
+    assert need > cap
+    rc = lib.tree_attention_noalloc(1, 51, 64, 20, 5, 128, FAKE, FAKE, FAKE, 65536, 65536, FAKE, FAKE, FAKE, FAKE,
+                                    C.c_float(0.1), FAKE, None)
+    _expect(rc, WS, ["static scratch"])
 
 
 def _post(B=2, V=100, mode=1, tau=0.7, tree=None, ws_bytes=1 << 20):
