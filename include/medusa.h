@@ -45,7 +45,8 @@ enum {
 };
 
 enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 };
-enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1 };
+enum { MEDUSA_GREEDY = 0, MEDUSA_TYPICAL = 1, MEDUSA_SAMPLED = 2 };
+enum { MEDUSA_SAMPLE_TYPICAL = 1, MEDUSA_SAMPLE_NUCLEUS = 2 };
 
 #define MEDUSA_MAX_TREE 64 /* nodes per tree, root included: one 64-bit mask word per node */
 
@@ -206,6 +207,56 @@ int kv_compact(int dtype, const medusa_tree* t, int n_layers, int B, int Hkv, in
                void* Kc, void* Vc, const void* Kt, const void* Vt, const int32_t* best,
                const int32_t* accept_len, int32_t* seq_len, const int32_t* tree_tokens,
                int32_t* out_tokens, int max_new, int32_t* n_out, int32_t* err_flag, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Sampling: the sampled root and the non-fast acceptance branch              */
+/* ------------------------------------------------------------------------- */
+/*
+ * Page "memory bandwidth bound (5) - Medusa": generate_candidates() (section
+ * 二.4) draws the root with get_typical_one_token / get_nucleus_one_token unless
+ * the temperature is 0 or `fast` is set (top_p defaults to 0.8, section 二.1);
+ * section 一.3 gives the typical allow set {x : p(x) > min(eps, delta exp(-H))};
+ * evaluate_posterior() (section 二.6) outside the fast branch keeps the first
+ * path of the longest accepted length.  The pages do not print those bodies;
+ * the reading implemented:
+ *   q = softmax(logits / temperature).  TYPICAL keeps {q > eta}, eta =
+ *   min(eps, delta exp(-H)), H = -sum q log(q + 1e-5) (an empty set leaves the
+ *   argmax); NUCLEUS keeps the smallest set of the most probable tokens whose
+ *   mass reaches top_p, ties with the last one included.  A draw is the allowed
+ *   token with the largest log q(x) - log(-log U(x)) (Gumbel-max; lowest index on
+ *   ties), U from Philox4x32-10 keyed by `seed`, counter (x / 4, position,
+ *   sequence, 0), output word x % 4, U = (2 (r >> 9) + 1) / 2^24.  `position`
+ *   is the absolute position of the token whose logits are sampled.
+ */
+typedef struct medusa_sampling {
+  int32_t kind;      /* MEDUSA_SAMPLE_TYPICAL or MEDUSA_SAMPLE_NUCLEUS */
+  float temperature; /* > 0 */
+  float eps, delta;  /* typical: posterior_threshold, posterior_alpha */
+  float top_p;       /* nucleus */
+  uint64_t seed;
+} medusa_sampling;
+
+/*
+ * One draw per row: out[r] drawn from logits[r*ldx .. r*ldx + V) (fp32, device)
+ * for sequence seq_id[r] (nullable: r) at position pos[r] (device int32 [M]).
+ * s is a host pointer read at the call.
+ */
+int medusa_sample_tokens(const medusa_sampling* s, int M, int V, const float* logits, int64_t ldx,
+                         const int32_t* seq_id, const int32_t* pos, int32_t* out, hipStream_t stream);
+
+/*
+ * Non-fast acceptance: one draw at every tree node u of sequence b (its logits
+ * row, position tree_pos[b, u], sequence b); a candidate is accepted when its
+ * token equals the draw at its parent (pads never); best = the first path of the
+ * longest accepted length (0 when none); sel_node = retrieve[best][a];
+ * next_root = the draw at sel_node.  Outputs and layouts as evaluate_posterior;
+ * tree_pos [B, T] int32 as tree_build_candidates writes it.
+ */
+size_t evaluate_posterior_sampled_workspace_size(int B, int T);
+int evaluate_posterior_sampled(const medusa_tree* t, int B, int V, const float* logits, const int32_t* tree_tokens,
+                               const int32_t* tree_pos, const medusa_sampling* s, int32_t* best,
+                               int32_t* accept_len, int32_t* sel_node, int32_t* next_root, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* Tree calibration                                                           */

@@ -186,6 +186,12 @@ typedef struct medusa_state {
    * a+1 tokens and a full output or cache sets err instead. */
   int32_t* done;
   int32_t stop_token;
+  /* Sampled generation (nullable, host pointer read at each call): prefill
+   * draws the root at the last prompt position instead of taking the argmax,
+   * and a step with mode MEDUSA_SAMPLED accepts by evaluate_posterior_sampled
+   * (the non-fast branch) and takes the draw at the selected node as the next
+   * root.  Null keeps the argmax root. */
+  const medusa_sampling* sampling;
 } medusa_state;
 
 /*
@@ -199,7 +205,9 @@ int medusa_prefill(const medusa_model* m, int B, int S, const int32_t* prompt, m
                    size_t ws_bytes, hipStream_t stream);
 
 /*
- * One verify iteration for B sequences sharing tree t:
+ * One verify iteration for B sequences sharing tree t (mode MEDUSA_GREEDY,
+ * MEDUSA_TYPICAL -- the fast branch, temperature/eps/delta used -- or
+ * MEDUSA_SAMPLED, which needs st->sampling and ignores temperature/eps/delta):
  *   Medusa heads + top-K on h_sel -> candidates -> forward of the T tree tokens
  *   -> acceptance -> KV compaction + token append -> h_sel, root for the next step.
  * best, accept_len and sel_node are written for every sequence; root and h_sel

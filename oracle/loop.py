@@ -19,18 +19,30 @@ Test infrastructure only (see ``oracle/__init__``).
 import numpy as np
 
 from .candidates import build_candidates
-from .decoder import forward, prefill
+from .decoder import forward, prefill, write_cache
 from .heads import medusa_heads_topk, root_token
-from .posterior import evaluate_posterior
+from .posterior import evaluate_posterior, evaluate_posterior_sampled_one
+from .sampling import draw
 from .update import accepted_tokens, appended_counts, kv_compact, kv_compact_counts
 
 
+def _draw_last(logits, sampling, seq_positions):
+    """The sampled root of every sequence from its last logits (position seq_positions[b])."""
+    s = sampling
+    return np.array([draw(logits[b], s["kind"], s["temperature"], s["eps"], s["delta"], s["top_p"], s["seed"], b,
+                          int(seq_positions[b]))[0] for b in range(logits.shape[0])], dtype=np.int64)
+
+
 def medusa_generate(params, heads, tree, prompt, n_steps, Lmax, mode, temperature=0.0,
-                    eps=0.09, delta=0.3, bf16=False, topk_hook=None, stop_token=None, max_new=None):
-    """Returns (tokens: list per sequence of appended tokens, per-step records)."""
+                    eps=0.09, delta=0.3, bf16=False, topk_hook=None, stop_token=None, max_new=None,
+                    sampling=None):
+    """Returns (tokens: list per sequence of appended tokens, per-step records).
+
+    ``sampling`` (dict kind, temperature, eps, delta, top_p, seed) selects the
+    non-``fast`` branch: sampled root and draw-matching acceptance (``mode`` ignored)."""
     logits, h, cK, cV, seq = prefill(params, prompt, Lmax, bf16=bf16)
     B = seq.shape[0]
-    root = root_token(logits[:, -1])
+    root = root_token(logits[:, -1]) if sampling is None else _draw_last(logits[:, -1], sampling, seq - 1)
     h_sel = h[:, -1]
     toks = [[] for _ in range(B)]
     done = np.zeros(B, dtype=bool)
@@ -41,7 +53,15 @@ def medusa_generate(params, heads, tree, prompt, n_steps, Lmax, mode, temperatur
             topk = topk_hook(step, topk, toks)
         tree_tokens, tree_pos, cart = build_candidates(tree, root, topk, seq)
         lg, hh, Kt, Vt = forward(params, tree_tokens, tree_pos, cK, cV, seq, tree["anc"], bf16=bf16)
-        best, a, sel, nr, _ = evaluate_posterior(tree, lg, tree_tokens, mode, temperature, eps, delta)
+        if sampling is None:
+            best, a, sel, nr, _ = evaluate_posterior(tree, lg, tree_tokens, mode, temperature, eps, delta)
+        else:
+            sm = sampling
+            rs = [evaluate_posterior_sampled_one(tree, lg[b], tree_tokens[b], tree_pos[b], sm["kind"],
+                                                 sm["temperature"], sm["eps"], sm["delta"], sm["top_p"], sm["seed"], b)
+                  for b in range(B)]
+            best, a, sel, nr = (np.array([r[k] for r in rs], dtype=np.int64)
+                                for k in ("best", "accept_len", "sel", "next_root"))
         counts = None
         if stop_token is None and max_new is None:
             for b, t in enumerate(accepted_tokens(cart, best, a)):
@@ -59,3 +79,21 @@ def medusa_generate(params, heads, tree, prompt, n_steps, Lmax, mode, temperatur
         records.append(dict(topk=topk, tree_tokens=tree_tokens, best=best, accept_len=a, sel=sel,
                             next_root=nr, counts=counts, seq_len=np.array(seq, copy=True)))
     return toks, records
+
+
+def plain_sampled_decode(params, prompt, n_new, Lmax, sampling, bf16=False):
+    """Plain autoregressive sampled decoding, one token per forward: the token at
+    position p + 1 is drawn from the logits at position p with the draw keyed by
+    (seed, sequence, p) -- the baseline the sampled Medusa loop must reproduce.
+    Returns [B, n_new]."""
+    logits, h, cK, cV, seq = prefill(params, prompt, Lmax, bf16=bf16)
+    tok = _draw_last(logits[:, -1], sampling, seq - 1)
+    out = [tok]
+    one = np.ones((1, 1), dtype=bool)
+    for _ in range(n_new - 1):
+        logits, h, Kn, Vn = forward(params, tok[:, None], seq[:, None], cK, cV, seq, one, bf16=bf16)
+        write_cache(cK, cV, Kn, Vn, seq)
+        tok = _draw_last(logits[:, -1], sampling, seq)
+        seq = seq + 1
+        out.append(tok)
+    return np.stack(out, axis=1)

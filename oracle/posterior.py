@@ -132,3 +132,38 @@ def evaluate_posterior(tree, logits, tree_tokens, mode, temperature=0.0, eps=0.0
     sel = np.array([r["sel"] for r in res], dtype=np.int64)
     nr = np.array([r["next_root"] for r in res], dtype=np.int64)
     return best, a, sel, nr, res
+
+
+def evaluate_posterior_sampled_one(tree, logits, tree_tokens, tree_pos, kind, temperature, eps=0.09, delta=0.3,
+                                   top_p=0.8, seed=0, seq=0):
+    """The non-``fast`` branch of section 二.6 for one sequence (the mask body is a
+    reading, see ``oracle.sampling``): one token is drawn at every tree node from its
+    logits (position = the node's position ``tree_pos``); a candidate is accepted when
+    it equals the token drawn at its parent (pads never); the accepted length of a path
+    is its number of leading accepted candidates; the chosen path is the first one of
+    the longest length (path 0 when nothing is accepted); the next root is the token
+    drawn at the selected node.
+
+    Returns dict(best, accept_len, sel, next_root, acc [P], draws [T], margins [T])."""
+    from .sampling import draw_rows
+    logits = np.asarray(logits, dtype=np.float64)
+    tree_tokens = np.asarray(tree_tokens, dtype=np.int64)
+    T, P, D = tree["T"], tree["P"], tree["D"]
+    retrieve, path_len = tree["retrieve"], tree["path_len"]
+    draws, margins = draw_rows(logits, kind, temperature, eps, delta, top_p, seed, [seq] * T,
+                               np.asarray(tree_pos, dtype=np.int64))
+    acc = np.zeros(P, dtype=np.int64)
+    for p in range(P):
+        n = 0
+        for j in range(1, D + 1):
+            if j >= path_len[p]:
+                break
+            if tree_tokens[retrieve[p, j]] != draws[retrieve[p, j - 1]]:
+                break
+            n += 1
+        acc[p] = n
+    a = int(acc.max()) if P else 0
+    best = 0 if a == 0 else int(np.flatnonzero(acc == a)[0])
+    sel = int(retrieve[best, a])
+    return dict(best=best, accept_len=a, sel=sel, next_root=int(draws[sel]), acc=acc, draws=draws,
+                margins=margins)

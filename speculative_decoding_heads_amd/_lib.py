@@ -13,7 +13,8 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmedusa.so")
 
 MEDUSA_F32, MEDUSA_BF16 = 0, 1
-GREEDY, TYPICAL = 0, 1
+GREEDY, TYPICAL, SAMPLED = 0, 1, 2
+SAMPLE_TYPICAL, SAMPLE_NUCLEUS = 1, 2
 EPI_F32, EPI_STORE, EPI_RESID, EPI_SILU_RESID_A, EPI_SWIGLU = 0, 1, 2, 3, 4
 MAX_TREE = 64
 
@@ -31,7 +32,8 @@ EXPORTED = [
     "medusa_prefill",
     "medusa_step_workspace_size", "medusa_step", "medusa_step_graph_create", "medusa_graph_launch",
     "medusa_graph_destroy", "medusa_step_fused_workspace_size", "medusa_step_fused",
-    "medusa_tree_from_acceptance", "medusa_head_hits",
+    "medusa_tree_from_acceptance", "medusa_head_hits", "medusa_sample_tokens",
+    "evaluate_posterior_sampled_workspace_size", "evaluate_posterior_sampled",
 ]
 
 
@@ -65,11 +67,24 @@ class TraceDesc(C.Structure):
                 ("x_mid", C.c_void_p), ("act", C.c_void_p)]
 
 
+class SamplingDesc(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("temperature", C.c_float), ("eps", C.c_float), ("delta", C.c_float),
+                ("top_p", C.c_float), ("seed", C.c_uint64)]
+
+
+def sampling_desc(sampling):
+    """medusa_sampling from a dict(kind, temperature, eps, delta, top_p, seed)."""
+    s = sampling
+    return SamplingDesc(int(s["kind"]), float(s["temperature"]), float(s.get("eps", 0.09)),
+                        float(s.get("delta", 0.3)), float(s.get("top_p", 0.8)), int(s.get("seed", 0)))
+
+
 class StateDesc(C.Structure):
     _fields_ = [("Kc", C.c_void_p), ("Vc", C.c_void_p), ("Lmax", C.c_int64), ("seq_len", C.c_void_p),
                 ("root", C.c_void_p), ("h_sel", C.c_void_p), ("out_tokens", C.c_void_p), ("max_new", C.c_int),
                 ("n_out", C.c_void_p), ("err", C.c_void_p), ("best", C.c_void_p), ("accept_len", C.c_void_p),
-                ("sel_node", C.c_void_p), ("done", C.c_void_p), ("stop_token", C.c_int32)]
+                ("sel_node", C.c_void_p), ("done", C.c_void_p), ("stop_token", C.c_int32),
+                ("sampling", C.POINTER(SamplingDesc))]
 
 
 _lib = None
@@ -124,6 +139,10 @@ def _declare(lib):
                                    _S, _P]),
         "medusa_tree_from_acceptance": (_I, [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, C.POINTER(C.c_double)]),
         "medusa_head_hits": (_I, [_I, _I, _I, _P, _P, _I, _P, _P, _P]),
+        "medusa_sample_tokens": (_I, [C.POINTER(SamplingDesc), _I, _I, _P, _L, _P, _P, _P, _P]),
+        "evaluate_posterior_sampled_workspace_size": (_S, [_I, _I]),
+        "evaluate_posterior_sampled": (_I, [_P, _I, _I, _P, _P, _P, C.POINTER(SamplingDesc), _P, _P, _P, _P, _P, _S,
+                                            _P]),
         "medusa_graph_launch": (_I, [_P, _P]),
         "medusa_graph_destroy": (_I, [_P]),
     }

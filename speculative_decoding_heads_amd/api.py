@@ -159,6 +159,36 @@ def evaluate_posterior(tree, logits, tree_tokens, mode, temperature=0.0, eps=0.0
     return tuple(outs)
 
 
+def sample_tokens(logits, sampling, pos, seq_id=None, out=None):
+    """medusa_sample_tokens: logits [M, V] fp32, pos [M] int32 (and seq_id [M] int32 or row index)
+    -> tokens [M] int32.  sampling: dict(kind, temperature, eps, delta, top_p, seed)."""
+    torch = _torch()
+    M, V = logits.shape
+    if logits.dtype != torch.float32 or pos.dtype != torch.int32 or pos.numel() != M:
+        raise MedusaError("sample_tokens: fp32 logits [M, V] and int32 positions [M] expected")
+    out = torch.empty(M, dtype=torch.int32, device=logits.device) if out is None else out
+    sd = L.sampling_desc(sampling)
+    check(lib().medusa_sample_tokens(C.byref(sd), M, V, ptr(logits), logits.stride(0), ptr(seq_id), ptr(pos),
+                                     ptr(out), stream_ptr()))
+    return out
+
+
+def evaluate_posterior_sampled(tree, logits, tree_tokens, tree_pos, sampling, outs=None, ws=None):
+    """Non-fast acceptance: logits [B,T,V] fp32, tree_tokens / tree_pos [B,T] int32
+    -> (best, accept_len, sel_node, next_root) int32 [B]."""
+    torch = _torch()
+    B, T, V = logits.shape
+    if T != tree.T or logits.dtype != torch.float32:
+        raise MedusaError("evaluate_posterior_sampled: logits must be fp32 [B, T, V] with T = tree nodes")
+    if outs is None:
+        outs = [torch.empty(B, dtype=torch.int32, device=logits.device) for _ in range(4)]
+    ws = L._ws(ws, lib().evaluate_posterior_sampled_workspace_size(B, T), logits.device)
+    sd = L.sampling_desc(sampling)
+    check(lib().evaluate_posterior_sampled(tree.handle, B, V, ptr(logits), ptr(tree_tokens), ptr(tree_pos),
+                                           C.byref(sd), *[ptr(o) for o in outs], ptr(ws), ws.numel(), stream_ptr()))
+    return tuple(outs)
+
+
 def kv_compact(tree, Kc, Vc, Kt, Vt, best, accept_len, seq_len, tree_tokens, out_tokens=None, n_out=None,
                err_flag=None):
     """Kc/Vc [NL,B,Hkv,Lmax,Dh], Kt/Vt [NL,B,Hkv,T,Dh]; updates Kc, Vc, seq_len, out_tokens, n_out in place."""

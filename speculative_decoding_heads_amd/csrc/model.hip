@@ -295,8 +295,16 @@ extern "C" int medusa_prefill(const medusa_model* m, int B, int S, const int32_t
     hipLaunchKernelGGL(add_i32_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, st->seq_len, B, Sc);
     CK(check_launch("prefill append"));
     if (c0 + Sc == S) {
-      CK(medusa_argmax_rows(B, m->vocab, p.logits + (size_t)(Sc - 1) * m->vocab, (int64_t)Sc * m->vocab, st->root,
-                            stream));
+      if (st->sampling) {
+        // the root drawn from the last prompt position's logits (position S - 1)
+        hipLaunchKernelGGL(fill_i32_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, p.pos, B, S - 1);
+        CK(check_launch("prefill root position"));
+        CK(medusa_sample_tokens(st->sampling, B, m->vocab, p.logits + (size_t)(Sc - 1) * m->vocab,
+                                (int64_t)Sc * m->vocab, nullptr, p.pos, st->root, stream));
+      } else {
+        CK(medusa_argmax_rows(B, m->vocab, p.logits + (size_t)(Sc - 1) * m->vocab, (int64_t)Sc * m->vocab,
+                              st->root, stream));
+      }
       // h_sel[b] = h[b, Sc-1]: gather with a constant selector
       int32_t* selbuf = p.tok;  // reuse: B entries
       hipLaunchKernelGGL(fill_i32_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, selbuf, B, Sc - 1);
@@ -339,6 +347,8 @@ size_t step_layout(const medusa_model* m, const medusa_tree* t, int B, int64_t L
   s.fws_bytes = fwd_layout(m, B, T, L_hint, nullptr, nullptr);
   s.fws = c.take(s.fws_bytes);
   s.pws_bytes = evaluate_posterior_workspace_size(B, T);
+  if (evaluate_posterior_sampled_workspace_size(B, T) > s.pws_bytes)
+    s.pws_bytes = evaluate_posterior_sampled_workspace_size(B, T);
   s.pws = c.take(s.pws_bytes);
   if (sb) *sb = s;
   return c.off;
@@ -358,6 +368,19 @@ int compact_state(const medusa_model* m, const medusa_tree* t, int B, medusa_sta
   return kv_compact_flags(m->dtype, t, m->n_layers, B, m->n_kv_heads, m->head_dim, st->Lmax, st->Kc, st->Vc, Kt, Vt,
                           st->best, st->accept_len, st->seq_len, tok, st->out_tokens, st->max_new, st->n_out, st->err,
                           appended, stream);
+}
+
+// Acceptance of a step: the fast rule (greedy / typical) or, for MEDUSA_SAMPLED,
+// the draw-matching non-fast branch; next_root goes to the step workspace.
+int accept_step(const medusa_model* m, const medusa_tree* t, int B, int mode, float temperature, float eps,
+                float delta, medusa_state* st, const StepBufs& s, hipStream_t stream) {
+  if (mode == MEDUSA_SAMPLED) {
+    MEDUSA_REQUIRE(st->sampling, MEDUSA_ERR_ARG, "step: mode MEDUSA_SAMPLED needs state sampling parameters");
+    return evaluate_posterior_sampled(t, B, m->vocab, s.logits, s.tok, s.pos, st->sampling, st->best,
+                                      st->accept_len, st->sel_node, s.next_root, s.pws, s.pws_bytes, stream);
+  }
+  return evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best,
+                            st->accept_len, st->sel_node, s.next_root, s.pws, s.pws_bytes, stream);
 }
 
 // The next step's inputs, for the sequences that appended this step's tokens:
@@ -417,8 +440,7 @@ extern "C" int medusa_step(const medusa_model* m, const medusa_tree* t, int B, i
   CK(tree_build_candidates(t, B, H, K, st->root, topk, st->seq_len, s.tok, s.pos, s.cart, stream));
   CK(medusa_forward(m, B, T, s.tok, s.pos, st->Kc, st->Vc, st->Lmax, L_hint, st->seq_len, s.Kt, s.Vt, t->dev->anc,
                     s.logits, s.h, s.fws, s.fws_bytes, stream));
-  CK(evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best, st->accept_len,
-                        st->sel_node, s.next_root, s.pws, s.pws_bytes, stream));
+  CK(accept_step(m, t, B, mode, temperature, eps, delta, st, s, stream));
   CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, s.appended, stream));
   CK(commit_step(m, B, T, s, st, stream));
   return MEDUSA_OK;
@@ -500,8 +522,7 @@ extern "C" int medusa_step_fused(const medusa_model* m, const medusa_tree* t, in
   // the heads on the final hidden state of every tree node (B*T rows)
   CK(medusa_heads_topk(m->dtype, B * T, m->d, m->vocab, H, K, s.h, m->medusa_w1, m->medusa_w2, f.topk_all, nullptr,
                        f.hws, f.hws_bytes, stream));
-  CK(evaluate_posterior(t, B, m->vocab, s.logits, s.tok, mode, temperature, eps, delta, st->best, st->accept_len,
-                        st->sel_node, s.next_root, s.pws, s.pws_bytes, stream));
+  CK(accept_step(m, t, B, mode, temperature, eps, delta, st, s, stream));
   CK(compact_state(m, t, B, st, s.Kt, s.Vt, s.tok, s.appended, stream));
   CK(commit_step(m, B, T, s, st, stream));
   hipLaunchKernelGGL(gather_topk_kernel, dim3(B), dim3(64), 0, stream, T, H * K, f.topk_all, st->sel_node,

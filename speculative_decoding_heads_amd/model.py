@@ -120,9 +120,11 @@ class Model:
 class State:
     """Device buffers of B sequences in generation (medusa_state)."""
 
-    def __init__(self, model, B, Lmax, max_new, stop_token=None):
+    def __init__(self, model, B, Lmax, max_new, stop_token=None, sampling=None):
         """stop_token: per-sequence stop (an int >= 0, or -1 for output/cache room only);
-        None keeps the plain behaviour (every step appends all accepted tokens)."""
+        None keeps the plain behaviour (every step appends all accepted tokens).
+        sampling: dict(kind, temperature, eps, delta, top_p, seed) for sampled generation
+        (the root drawn at prefill and steps with mode SAMPLED); None keeps the argmax root."""
         torch = _torch()
         dev = model.device
         i32 = lambda *s: torch.zeros(s, dtype=torch.int32, device=dev)
@@ -136,9 +138,11 @@ class State:
         self.best, self.accept_len, self.sel_node = i32(B), i32(B), i32(B)
         self.done = i32(B) if stop_token is not None else None
         self.stop_token = -1 if stop_token is None else int(stop_token)
+        self.sampling = L.sampling_desc(sampling) if sampling is not None else None
         self.desc = L.StateDesc(ptr(self.Kc), ptr(self.Vc), Lmax, ptr(self.seq_len), ptr(self.root), ptr(self.h_sel),
                                 ptr(self.out_tokens), max_new, ptr(self.n_out), ptr(self.err), ptr(self.best),
-                                ptr(self.accept_len), ptr(self.sel_node), ptr(self.done), self.stop_token)
+                                ptr(self.accept_len), ptr(self.sel_node), ptr(self.done), self.stop_token,
+                                C.pointer(self.sampling) if self.sampling is not None else None)
 
 
 def prefill(model, state, prompt, ws=None):

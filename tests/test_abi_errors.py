@@ -104,3 +104,19 @@ def test_kv_compact_errors():
     _expect(_compact(dtype=1, Dh=4), UNSUP, ["16 bytes"])
     _expect(_compact(out_tokens=FAKE, n_out=None, max_new=8), ARG, ["needs n_out"])
     _expect(_compact(), ARG, ["null tree"])
+
+
+def test_sampling_calls_errors():
+    from speculative_decoding_heads_amd._lib import SamplingDesc
+    lib = _lib()
+    good = SamplingDesc(1, 0.7, 0.09, 0.3, 0.8, 1)
+    _expect(lib.medusa_sample_tokens(None, 4, 100, FAKE, 100, None, FAKE, FAKE, None), ARG, ["null parameters"])
+    _expect(lib.medusa_sample_tokens(C.byref(SamplingDesc(3, 0.7, 0.09, 0.3, 0.8, 1)), 4, 100, FAKE, 100, None,
+                                     FAKE, FAKE, None), ARG, ["kind 3"])
+    _expect(lib.medusa_sample_tokens(C.byref(SamplingDesc(2, 0.0, 0.09, 0.3, 0.8, 1)), 4, 100, FAKE, 100, None,
+                                     FAKE, FAKE, None), ARG, ["temperature"])
+    _expect(lib.medusa_sample_tokens(C.byref(good), 4, 100, FAKE, 99, None, FAKE, FAKE, None), ARG, ["bad sizes"])
+    _expect(lib.medusa_sample_tokens(C.byref(good), 4, 100, FAKE, 100, None, None, FAKE, None), ARG,
+            ["null pointer"])
+    _expect(lib.evaluate_posterior_sampled(None, 2, 100, FAKE, FAKE, FAKE, C.byref(good), FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, 1 << 20, None), ARG, ["null tree"])
