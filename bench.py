@@ -35,7 +35,16 @@ Also measured (same JSON line):
                  weights per call), against 8 TB/s
   kv_compact     the compaction call at batch 8, prefix 65536 (one layer)
   tiny_fp32_step the 2-layer fp32 model's verify step (launch-bound): steps/s, tok/s
-  cpu_baseline   the oracle on the host cores on a bounded sample of the same step
+  sampled_step   the same 7B step with sampled (non-fast) acceptance: a typical draw at
+                 every tree node, the next root drawn at the selected node
+  read_ceiling   the library's streaming-read kernel over 4 GiB: the practical HBM read
+                 rate; every memory-bound entry also reports frac_of_achievable against it
+  cpu_baseline   the oracle on the host cores on a bounded sample of the same step, plus
+                 the oracle's time on each of the other workloads (oracle_by_config)
+
+Short kernels (attention at small prefixes, KV compaction, the tiny step) are timed as
+many back-to-back launches captured in one HIP graph, so the figures are kernel times,
+not host launch rates.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
 python bench.py --roofline-only      the dominant-kernel launches and a 256 MiB copy
@@ -44,6 +53,11 @@ python bench.py --attn-traffic-only  the batch-8 / prefix-65536 attention launch
                                      256 MiB copy only, for rocprofv3 --pmc
 python bench.py --traffic-from FETCH_DIR WRITE_DIR
                                      turn the two counter runs into the traffic file
+python bench.py --heads-only         the heads on 512 tree-node rows (the square-tile
+                                     product) only, for rocprofv3 --pmc
+python bench.py --summarize-trace DIR
+                                     per-kernel, per-launch-shape table (markdown) of a
+                                     rocprofv3 --kernel-trace output directory
 """
 import argparse
 import json
@@ -79,6 +93,15 @@ def parse():
     p.add_argument("--roofline-only", action="store_true")
     p.add_argument("--attn-traffic-only", action="store_true")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--heads-only", action="store_true")
+    p.add_argument("--attn-case", metavar="B,L[,HKV]",
+                   help="time one tree-attention case alone (32 query heads x 128, the seeded 64-node tree) as "
+                        "back-to-back launches in one HIP graph, for a kernel trace of that case")
+    p.add_argument("--summarize-trace", metavar="DIR")
+    p.add_argument("--trace-window", metavar="KERNEL:N",
+                   help="with --summarize-trace: only the kernels between the N-th and (N+1)-th launch of KERNEL")
+    p.add_argument("--trace-runs", metavar="KERNEL",
+                   help="with --summarize-trace: consecutive runs of KERNEL launches with one grid, in trace order")
     p.add_argument("--sweep", type=str, default="4096,16384,65536",
                    help="longer prefixes at which the same step is also timed ('' for none)")
     return p.parse_args()
@@ -102,6 +125,122 @@ class Timer:
     def ms(self):
         self.e.synchronize()
         return self.s.elapsed_time(self.e)
+
+
+def graph_time_us(calls, reps=5):
+    """Microseconds per call of `calls` (a list of no-argument launch functions that
+    allocate nothing), all captured back to back into one HIP graph and replayed `reps`
+    times after one warm-up replay, timed with HIP events on the replaying stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for f in calls:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    with Timer() as t:
+        for _ in range(reps):
+            g.replay()
+    us = t.ms() * 1e3 / (reps * len(calls))
+    del g
+    return us
+
+
+def read_ceiling(dev, nbytes=4 << 30, reps=10):
+    """The library's streaming-read kernel over nbytes (> the 256 MB last-level cache):
+    GB/s of 10 back-to-back passes, 2048 workgroups (8 per CU)."""
+    import torch
+    from speculative_decoding_heads_amd._lib import check, lib, ptr, stream_ptr
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(2048, dtype=torch.int32, device=dev)
+
+    def one():
+        check(lib().medusa_read_probe(ptr(buf), nbytes, 2048, ptr(sink), stream_ptr()))
+
+    for _ in range(2):
+        one()
+    torch.cuda.synchronize()
+    with Timer() as t:
+        for _ in range(reps):
+            one()
+    ms = t.ms() / reps
+    del buf
+    torch.cuda.empty_cache()
+    return {"kernel": "read_probe_kernel (16-byte loads, 2048 workgroups)", "bytes": nbytes,
+            "us": round(ms * 1e3, 2), "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def _short_kernel_name(name):
+    for junk in ("void ", "medusa::", "(anonymous namespace)::", "at::native::"):
+        name = name.replace(junk, "")
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # drop the parameter list
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            cut = i
+            break
+    return name[:cut][:80]
+
+
+def summarize_trace(d, window=None, runs=None):
+    """Markdown tables of a rocprofv3 kernel trace: per kernel and launch shape (grid in
+    work-items), calls, average / min / max microseconds and share of the kernel time;
+    `window` = (kernel, n) restricts it to the dispatches between the n-th and (n+1)-th
+    launch of that kernel (one step) and adds the window's wall time; `runs` = kernel
+    lists the consecutive runs of that kernel's launches with one grid, in trace order."""
+    import csv
+    import glob
+    rows = []
+    for fn in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit("no kernel_trace.csv under %s" % d)
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        r["name"] = _short_kernel_name(r["Kernel_Name"])
+        r["grid"] = "%s x %s x %s" % (r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"])
+        r["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = []
+    if runs:
+        out += ["| Run | `%s` grid (work-items) | Launches | Avg (us) | Min (us) | Max (us) |" % runs,
+                "|---:|---|---:|---:|---:|---:|"]
+        seq, cur = [], None
+        for r in rows:
+            if runs not in r["name"]:
+                continue
+            if cur is None or cur[0] != r["grid"]:
+                cur = (r["grid"], [])
+                seq.append(cur)
+            cur[1].append(r["us"])
+        for i, (grid, v) in enumerate(seq):
+            out.append("| %d | %s | %d | %.2f | %.2f | %.2f |" % (i, grid, len(v), sum(v) / len(v), min(v), max(v)))
+        print("\n".join(out))
+        return
+    if window:
+        kname, n = window.rsplit(":", 1)
+        idx = [i for i, r in enumerate(rows) if kname in r["name"]]
+        n = int(n)
+        if n + 1 >= len(idx):
+            raise SystemExit("fewer than %d launches of %s" % (n + 2, kname))
+        rows = rows[idx[n]:idx[n + 1]]
+        wall = (int(rows[-1]["End_Timestamp"]) - int(rows[0]["Start_Timestamp"])) / 1e3
+        out.append("Window: launches %d..%d of the trace, between launches %d and %d of `%s`; wall %.1f us, kernel "
+                   "time %.1f us.\n" % (idx[n], idx[n + 1] - 1, n, n + 1, kname, wall, sum(r["us"] for r in rows)))
+    groups = {}
+    for r in rows:
+        groups.setdefault((r["name"], r["grid"]), []).append(r["us"])
+    total = sum(sum(v) for v in groups.values())
+    out += ["| Kernel | Grid (work-items) | Calls | Avg (us) | Min (us) | Max (us) | Total (us) | % of kernel time |",
+            "|---|---|---:|---:|---:|---:|---:|---:|"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append("| `%s` | %s | %d | %.2f | %.2f | %.2f | %.1f | %.1f |" % (
+            name.replace("|", "/"), grid, len(v), sum(v) / len(v), min(v), max(v), sum(v), 100 * sum(v) / total))
+    print("\n".join(out))
 
 
 def gemm_bytes(M, N, K, out_bytes):
@@ -172,13 +311,16 @@ def main():
     if args.traffic_from:
         traffic_from(*args.traffic_from)
         return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.trace_window, args.trace_runs)
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
 
     from speculative_decoding_heads_amd import api
-    from speculative_decoding_heads_amd._lib import EPI_F32, EPI_RESID, EPI_SWIGLU, TYPICAL, lib
+    from speculative_decoding_heads_amd._lib import EPI_F32, EPI_RESID, EPI_SWIGLU, SAMPLE_TYPICAL, SAMPLED, TYPICAL, lib
     from speculative_decoding_heads_amd.model import (Model, State, StepGraph, init_topk_carry, prefill, step,
                                                       step_fused, step_fused_workspace_size, step_workspace_size)
     from workloads import (SevenBConfig, acceptance_table, model_weights_torch, prompt_tokens, seeded_tree_choices,
@@ -191,9 +333,15 @@ def main():
     if args.attn_traffic_only:
         attn_traffic_run(dev)
         return
+    if args.heads_only:
+        heads_only_run(dev)
+        return
+    if args.attn_case:
+        attn_case_run(dev, *[int(x) for x in args.attn_case.split(",")])
+        return
     log("generating %d-layer 7B-shaped weights on device" % NL)
     params, heads = model_weights_torch(cfg, 1, dev, torch.bfloat16, n_layers=NL)
-    sample_layers = [{k: v for k, v in params["layers"][i].items()} for i in range(min(4, NL))]
+    sample_layers = [{k: v for k, v in params["layers"][i].items()} for i in range(min(8, NL))]
     sweep_L = [int(x) for x in args.sweep.split(",") if x.strip()]
     model = Model(params, heads, max_pos=max([args.prefix] + sweep_L) + 512)
     for l in params["layers"]:
@@ -238,14 +386,20 @@ def main():
     log("eager: warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
         one_step()
+        # the accumulation is warmed up too: the first launch of a torch kernel loads its
+        # code object (tens of ms), which must not land in the timed window
+        acc_sum += st.accept_len
     torch.cuda.synchronize()
+    acc_sum.zero_()
     t0 = time.perf_counter()
     with Timer() as te:
         for _ in range(args.steps):
             one_step()
+            acc_sum += st.accept_len
     eager_ms = te.ms() / args.steps
     eager_wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     log("eager step %.3f ms" % eager_ms)
+    mean_tokens = float(acc_sum.sum()) / (args.steps * B) + 1.0
 
     # the same step captured once into a HIP graph and replayed
     gstream = torch.cuda.Stream()
@@ -262,25 +416,64 @@ def main():
             graph_step()
         torch.cuda.synchronize()
         log("timing %d steps" % args.steps)
-        acc_sum.zero_()
         t0 = time.perf_counter()
         with Timer() as tm:
             for _ in range(args.steps):
                 graph_step()
-                acc_sum += st.accept_len
-        step_ms = tm.ms() / args.steps
-        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph_ms = tm.ms() / args.steps
+        graph_wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     torch.cuda.synchronize()
-    graph_ms = step_ms
-    launch = "HIP graph replay of one step (eager launches: %.4f ms/step)" % eager_ms
-    if eager_ms < graph_ms:
-        # the reported figure is the faster of the two launch modes, both timed above
-        step_ms = eager_ms
-        wall_ms = eager_wall_ms
+    # order check: short alternating blocks of both modes after the main windows
+    alt = {"eager": [], "graph": []}
+    for _ in range(2):
+        with Timer() as ta:
+            for _ in range(5):
+                one_step()
+        alt["eager"].append(round(ta.ms() / 5, 4))
+        with torch.cuda.stream(gstream):
+            with Timer() as tb:
+                for _ in range(5):
+                    graph_step()
+            alt["graph"].append(round(tb.ms() / 5, 4))
+        torch.cuda.synchronize()
+    if eager_ms <= graph_ms:
+        # the reported figure is the faster of the two launch modes, both timed over the K steps
+        step_ms, wall_ms = eager_ms, eager_wall_ms
         launch = "eager launches, one library call per step (HIP graph replay: %.4f ms/step)" % graph_ms
+    else:
+        step_ms, wall_ms = graph_ms, graph_wall_ms
+        launch = "HIP graph replay of one step (eager launches: %.4f ms/step)" % eager_ms
+    launch_detail = {"eager_ms": round(eager_ms, 4), "graph_ms": round(graph_ms, 4),
+                     "alternating_5_step_blocks_ms": alt}
     assert int(st.err[0]) == 0, "state error flag set"
-    mean_tokens = float(acc_sum.sum()) / (args.steps * B) + 1.0
     steps_per_s = 1e3 / step_ms
+
+    # sampled (non-fast) acceptance: a typical draw at every tree node, the next root
+    # drawn at the selected node (eager launches, the same prefix reset)
+    samp = dict(kind=SAMPLE_TYPICAL, temperature=tau, eps=eps, delta=delta, top_p=0.8, seed=1234)
+    sst = State(model, B, Lmax, 64, sampling=samp)
+    for name in ("Kc", "Vc", "root", "h_sel"):
+        getattr(sst, name).copy_(getattr(st, name))
+
+    def sampled_step():
+        sst.seq_len.copy_(base_seq)
+        sst.n_out.zero_()
+        step(model, tree, sst, SAMPLED, L_hint=Lmax, ws=ws)
+
+    for _ in range(args.warmup):
+        sampled_step()
+        acc_sum += sst.accept_len
+    torch.cuda.synchronize()
+    acc_sum.zero_()
+    with Timer() as tsm:
+        for _ in range(args.steps):
+            sampled_step()
+            acc_sum += sst.accept_len
+    sampled_ms = tsm.ms() / args.steps
+    sampled_tokens = float(acc_sum.sum()) / (args.steps * B) + 1.0
+    assert int(sst.err[0]) == 0, "state error flag set"
+    log("sampled step %.3f ms" % sampled_ms)
+    del sst
 
     # fused draft + verify: the heads on all 64 tree nodes inside the step, the
     # next candidates taken at the selected node (eager launches, same prefix reset)
@@ -423,32 +616,10 @@ def main():
 
     # ---- tree attention alone
     def attn_case(Bc, L, reps, Hkv=8):
-        q = torch_normal((Bc, T, 32, Dh), 1.0, 11, dev, torch.bfloat16)
-        # rotate over > 1 GB of distinct K/V at small L so the 256 MB last-level cache cannot serve them
-        nbuf = max(1, min(128, int(1.2e9 // (Bc * Hkv * L * Dh * 2 * 2)) + 1))
-        Ks = [torch_normal((Bc, Hkv, L, Dh), 1.0, 20 + i, dev, torch.bfloat16) for i in range(nbuf)]
-        Vs = [torch_normal((Bc, Hkv, L, Dh), 1.0, 40 + i, dev, torch.bfloat16) for i in range(nbuf)]
-        Kt = torch_normal((Bc, Hkv, T, Dh), 1.0, 60, dev, torch.bfloat16)
-        Vt = torch_normal((Bc, Hkv, T, Dh), 1.0, 61, dev, torch.bfloat16)
-        seq = torch.full((Bc,), L, dtype=torch.int32, device=dev)
-        out = torch.empty_like(q)
-        aws = torch.empty(max(1, api.tree_attention_workspace_size(1, Bc, T, 32, Hkv, Dh, L)), dtype=torch.uint8,
-                          device=dev)
-        for i in range(nbuf):
-            api.tree_attention(q, Ks[i], Vs[i], seq, Kt, Vt, tree, Dh ** -0.5, out=out, ws=aws)
-        torch.cuda.synchronize()
-        with Timer() as ta:
-            for r in range(reps):
-                i = r % nbuf
-                api.tree_attention(q, Ks[i], Vs[i], seq, Kt, Vt, tree, Dh ** -0.5, out=out, ws=aws)
-        ms = ta.ms() / reps
-        nbytes = Bc * Hkv * L * Dh * 2 * 2 + Bc * Hkv * T * Dh * 2 * 2 + 2 * Bc * T * 32 * Dh * 2
-        del Ks, Vs
-        torch.cuda.empty_cache()
-        return ms, nbytes
+        return attn_case_time(dev, tree, Bc, L, reps, Hkv)
 
     a64_ms, a64_b = attn_case(8, 65536, args.attn_reps)
-    a1k_ms, a1k_b = attn_case(1, 1024, args.attn_reps * 5)
+    a1k_ms, a1k_b = attn_case(1, 1024, 128)
     # the 7B-shaped model's attention (32 heads, no KV-head sharing) at a long prefix
     amha_ms, amha_b = attn_case(1, 65536, args.attn_reps, Hkv=32)
     amha_gbs = amha_b / (amha_ms * 1e-3) / 1e9
@@ -483,8 +654,10 @@ def main():
         for Ls in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
             if Bc == 8 and Ls == 65536:
                 ms_, b_ = a64_ms, a64_b
+            elif Bc == 1 and Ls == 1024:
+                ms_, b_ = a1k_ms, a1k_b
             else:
-                ms_, b_ = attn_case(Bc, Ls, max(5, args.attn_reps // 2))
+                ms_, b_ = attn_case(Bc, Ls, max(10, min(128, int(2e6 // Ls))))
             g_ = b_ / (ms_ * 1e-3) / 1e9
             attn_sweep["B%d_L%d" % (Bc, Ls)] = {"us": round(ms_ * 1e3, 2), "achieved": round(g_, 1),
                                                 "frac": round(g_ / HBM_PEAK_GBS, 4), "bytes": b_}
@@ -522,43 +695,63 @@ def main():
     # ---- KV compaction after acceptance: one layer, batch 8, 8 KV heads, prefix 65536,
     # accepted length a ~ U{0..4} on a seeded leaf path long enough for it
     rng_c = np.random.default_rng(5)
-    Bc, Lc = 8, 65536
-    Kc5 = torch.zeros((1, Bc, 8, Lc + 128, Dh), dtype=torch.bfloat16, device=dev)
-    Vc5 = torch.zeros_like(Kc5)
-    Kt5 = torch_normal((1, Bc, 8, T, Dh), 1.0, 90, dev, torch.bfloat16)
-    Vt5 = torch_normal((1, Bc, 8, T, Dh), 1.0, 91, dev, torch.bfloat16)
-    best_np = rng_c.integers(0, tree.P, Bc)
-    acc_np = np.array([rng_c.integers(0, min(5, int(tree.path_len[b_]))) for b_ in best_np])
-    best5 = torch.from_numpy(best_np.astype(np.int32)).to(dev)
-    acc5 = torch.from_numpy(acc_np.astype(np.int32)).to(dev)
-    seq5_0 = torch.full((Bc,), Lc, dtype=torch.int32, device=dev)
-    seq5 = seq5_0.clone()
-    tt5 = torch.zeros((Bc, T), dtype=torch.int32, device=dev)
+    n_comp = 100
 
-    def compact5():
-        seq5.copy_(seq5_0)
-        api.kv_compact(tree, Kc5, Vc5, Kt5, Vt5, best5, acc5, seq5, tt5)
+    def compact_case(NLc, Bc, Hkvc, Lc):
+        """n_comp back-to-back compaction calls in one captured graph (each call appends its
+        rows after the previous call's, so the cache has room for all of them)."""
+        Kc5 = torch.zeros((NLc, Bc, Hkvc, Lc + 6 * n_comp + 8, Dh), dtype=torch.bfloat16, device=dev)
+        Vc5 = torch.zeros_like(Kc5)
+        Kt5 = torch_normal((NLc, Bc, Hkvc, T, Dh), 1.0, 90, dev, torch.bfloat16)
+        Vt5 = torch_normal((NLc, Bc, Hkvc, T, Dh), 1.0, 91, dev, torch.bfloat16)
+        best_np = rng_c.integers(0, tree.P, Bc)
+        acc_np = np.array([rng_c.integers(0, min(5, int(tree.path_len[b_]))) for b_ in best_np])
+        best5 = torch.from_numpy(best_np.astype(np.int32)).to(dev)
+        acc5 = torch.from_numpy(acc_np.astype(np.int32)).to(dev)
+        seq5 = torch.full((Bc,), Lc, dtype=torch.int32, device=dev)
+        tt5 = torch.zeros((Bc, T), dtype=torch.int32, device=dev)
+        calls = [lambda: api.kv_compact(tree, Kc5, Vc5, Kt5, Vt5, best5, acc5, seq5, tt5)] * n_comp
+        us = graph_time_us(calls, reps=1)
+        moved = int(NLc * Hkvc * Dh * 2 * 2 * 2 * int((acc_np + 1).sum()))  # K and V rows, read + write
+        del Kc5, Vc5
+        torch.cuda.empty_cache()
+        return {"us_per_call": round(us, 2), "bytes_moved": moved, "achieved": round(moved / (us * 1e-6) / 1e9, 1),
+                "unit": "GB/s", "accepted_rows": (acc_np + 1).tolist()}
 
-    for _ in range(3):
-        compact5()
-    torch.cuda.synchronize()
-    with Timer() as tc5:
-        for _ in range(20):
-            compact5()
-    compact_us = tc5.ms() / 20 * 1e3
-    compact_bytes = int(2 * 2 * 8 * Dh * 2 * int((acc_np + 1).sum()))
-    log("kv_compact B8 L65536 (1 layer): %.1f us per call (with the length reset)" % compact_us)
-    del Kc5, Vc5
-    torch.cuda.empty_cache()
+    compact5 = compact_case(1, 8, 8, 65536)
+    compact5["case"] = "1 layer, batch 8, 8 KV heads x 128, prefix 65536, a ~ U{0..4} on seeded leaves"
+    compact_step = compact_case(NL, 1, cfg.n_kv_heads, args.prefix)
+    compact_step["case"] = "%d layers, batch 1, 32 KV heads x 128, prefix %d (the verify step's compaction)" % (
+        NL, args.prefix)
+    log("kv_compact: %.2f us (batch 8, 1 layer), %.2f us (the step's %d layers)" % (
+        compact5["us_per_call"], compact_step["us_per_call"], NL))
 
     # ---- the tiny fp32 step (2-layer decoder, d 64, 2 heads, the 2-head tree): launch-bound
     tiny = tiny_step_rate(dev)
     log("tiny fp32 step: %.1f us, %.0f steps/s" % (tiny["us_per_step"], tiny["steps_per_s"]))
 
+    # ---- the practical HBM read rate: every memory-bound figure also against it
+    ceil = read_ceiling(dev)
+    ach = ceil["achieved"]
+    log("streaming read ceiling: %.1f GB/s" % ach)
+    foa = lambda gbs: round(gbs / ach, 4)
+    for case in attn_sweep.values():
+        case["frac_of_achievable"] = foa(case["achieved"])
+    for case in heads_b.values():
+        case["frac_of_achievable"] = foa(case["achieved"])
+    # the whole step's algorithmic bytes: every projection's weights, activations and
+    # outputs, the heads' weights, and per layer the attention's cache, tree K/V, q and out
+    attn_layer_b = B * cfg.n_kv_heads * (args.prefix * Dh * 2 * 2 + T * Dh * 2 * 2) + 2 * B * T * Hq * Dh * 2
+    step_b = gemm_b + hbytes + NL * attn_layer_b
+    step_gbs = step_b / (step_ms * 1e-3) / 1e9
+
     # ---- oracle on the host cores, bounded sample of the same step
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(params, heads, sample_layers, model, cfg, tree, prompt, args.prefix, dev)
+        gpu_ref = {"tiny_us": tiny["us_per_step"], "attn_b1_us": round(a1k_ms * 1e3, 2),
+                   "heads_b1_us": heads_b["B1"]["us"], "attn_b8_us": round(a64_ms * 1e3, 2),
+                   "compact_us": compact5["us_per_call"]}
+        cpu = cpu_baseline(params, heads, sample_layers, model, cfg, tree, prompt, args.prefix, dev, gpu_ref)
 
     out = {
         "metric": "tree-verify steps/s (7B-shaped verify step, prefix 1024)",
@@ -581,21 +774,36 @@ def main():
         "accepted_tok_per_s": round(steps_per_s * mean_tokens, 2),
         "wall_ms_per_step": round(wall_ms, 4),
         "launch": launch,
+        "launch_detail": launch_detail,
         "roofline": {"kernel": "gemm_dma_kernel<2,3,7>: gate/up projection, M 64, N 22016, K 4096, SwiGLU",
                      "bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "achievable": ach, "frac_of_achievable": foa(gu_gbs),
                      "bytes_per_launch": gu_b, "us_per_launch": round(gu_us, 3)},
+        "step_hbm": {"bytes_per_step": step_b, "achieved": round(step_gbs, 1), "unit": "GB/s",
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4), "frac_of_achievable": foa(step_gbs),
+                     "note": "algorithmic bytes of the whole step (projection and head weights, activations, "
+                             "attention cache and tree K/V) over the reported step time"},
+        "read_ceiling": ceil,
         "step_projections": {"kernels": "gemm_dma_kernel + resid_rmsnorm_kernel: every projection of one step",
                              "achieved": round(gemm_gbs, 1), "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
-                             "bytes_per_step": gemm_b, "ms_per_step": round(gemm_ms, 4),
-                             "calls": len(gemm_launches)},
+                             "frac_of_achievable": foa(gemm_gbs), "bytes_per_step": gemm_b,
+                             "ms_per_step": round(gemm_ms, 4), "calls": len(gemm_launches)},
         "tree_attention": {
             "B8_L65536": {"us": round(a64_ms * 1e3, 2), "achieved": round(a64_gbs, 1), "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": round(a64_gbs / HBM_PEAK_GBS, 4), "bytes": a64_b},
+                          "unit": "GB/s", "frac": round(a64_gbs / HBM_PEAK_GBS, 4),
+                          "frac_of_achievable": foa(a64_gbs), "bytes": a64_b},
             "B1_L1024": {"us": round(a1k_ms * 1e3, 2), "achieved": round(a1k_gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(a1k_gbs / HBM_PEAK_GBS, 4), "bytes": a1k_b},
+                         "unit": "GB/s", "frac": round(a1k_gbs / HBM_PEAK_GBS, 4),
+                         "frac_of_achievable": foa(a1k_gbs), "bytes": a1k_b},
             "B1_MHA32_L65536": {"us": round(amha_ms * 1e3, 2), "achieved": round(amha_gbs, 1), "peak": HBM_PEAK_GBS,
-                                "unit": "GB/s", "frac": round(amha_gbs / HBM_PEAK_GBS, 4), "bytes": amha_b}},
+                                "unit": "GB/s", "frac": round(amha_gbs / HBM_PEAK_GBS, 4),
+                                "frac_of_achievable": foa(amha_gbs), "bytes": amha_b},
+            "timing": "launches captured back to back in one HIP graph, K/V rotated over > 1 GB at short prefixes"},
+        "sampled_step": {"ms_per_step": round(sampled_ms, 4), "steps_per_s": round(1e3 / sampled_ms, 3),
+                         "accepted_tokens_per_step": round(sampled_tokens, 3),
+                         "sampling": "typical draws (tau 0.7, eps 0.09, delta 0.3, Philox seed 1234) at every tree "
+                                     "node, candidates accepted when equal to the draw at their parent, eager launches"},
         "prefix_sweep": sweep,
         "tree_size_sweep": {"acceptance": "synthetic table: depth d in top-10 with probability 0.75 * 0.85^d, "
                                           "ranks in proportion to 0.5^r (not from the pages)",
@@ -613,13 +821,75 @@ def main():
                                  "unit": "GB/s", "cases": attn_sweep},
         "heads_topk_candidates": {"kernels": "medusa_heads_topk (W1, W2 products + top-10) + tree_build_candidates",
                                   "bound": "hbm", "peak": HBM_PEAK_GBS, "cases": heads_b},
-        "kv_compact": {"case": "1 layer, batch 8, 8 KV heads x 128, prefix 65536, a ~ U{0..4}",
-                       "us_per_call": round(compact_us, 2), "bytes_moved": compact_bytes,
-                       "note": "launch-bound: the time includes a 32-byte length reset"},
+        "kv_compact": {"kernels": "compact_kv_kernel + compact_finalize_kernel, %d calls captured in one graph"
+                                  % n_comp, "bound": "latency (a few hundred KB per call)",
+                       "B8_L65536_1layer": compact5, "step_32layers": compact_step},
         "tiny_fp32_step": tiny,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def attn_case_time(dev, tree, Bc, L, reps, Hkv=8, Dh=128):
+    """(ms per call, algorithmic bytes) of tree_attention at batch Bc, prefix L, 32 query /
+    Hkv KV heads x Dh: `reps` (at least one full rotation of the K/V sets) launches captured
+    in one HIP graph; at short prefixes the launches rotate over > 1 GB of distinct K/V so
+    the 256 MB last-level cache cannot serve them."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from workloads import torch_normal
+    T = tree.T
+    q = torch_normal((Bc, T, 32, Dh), 1.0, 11, dev, torch.bfloat16)
+    nbuf = max(1, min(128, int(1.2e9 // (Bc * Hkv * L * Dh * 2 * 2)) + 1))
+    Ks = [torch_normal((Bc, Hkv, L, Dh), 1.0, 20 + i, dev, torch.bfloat16) for i in range(nbuf)]
+    Vs = [torch_normal((Bc, Hkv, L, Dh), 1.0, 40 + i, dev, torch.bfloat16) for i in range(nbuf)]
+    Kt = torch_normal((Bc, Hkv, T, Dh), 1.0, 60, dev, torch.bfloat16)
+    Vt = torch_normal((Bc, Hkv, T, Dh), 1.0, 61, dev, torch.bfloat16)
+    seq = torch.full((Bc,), L, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    aws = torch.empty(max(1, api.tree_attention_workspace_size(1, Bc, T, 32, Hkv, Dh, L)), dtype=torch.uint8,
+                      device=dev)
+    n = max(reps, nbuf)
+    calls = [lambda i=i: api.tree_attention(q, Ks[i % nbuf], Vs[i % nbuf], seq, Kt, Vt, tree, Dh ** -0.5, out=out,
+                                            ws=aws) for i in range(n)]
+    ms = graph_time_us(calls, reps=3) * 1e-3
+    nbytes = Bc * Hkv * L * Dh * 2 * 2 + Bc * Hkv * T * Dh * 2 * 2 + 2 * Bc * T * 32 * Dh * 2
+    del Ks, Vs
+    torch.cuda.empty_cache()
+    return ms, nbytes
+
+
+def attn_case_run(dev, Bc, L, Hkv=8):
+    """One attention case alone (for a per-case kernel trace): its time per call and GB/s."""
+    from speculative_decoding_heads_amd import api
+    from workloads import seeded_tree_choices
+    tree = api.Tree(seeded_tree_choices(0))
+    ms, nbytes = attn_case_time(dev, tree, Bc, L, max(10, min(128, int(2e6 // L))), Hkv)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"case": "B%d_L%d_Hkv%d" % (Bc, L, Hkv), "us": round(ms * 1e3, 2), "bytes": nbytes,
+                      "achieved": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+
+
+def heads_only_run(dev):
+    """For rocprofv3 --pmc: the Medusa heads (d 4096, V 32000, 4 heads, top-10) on 512 hidden
+    states -- every node of 8 sequences' 64-node trees, the square-tile products -- three times."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import lib
+    from workloads import SevenBConfig, torch_normal
+    cfg = SevenBConfig
+    W1 = torch_normal((cfg.n_medusa, cfg.d, cfg.d), 0.02, 3001, dev, torch.bfloat16)
+    W2 = torch_normal((cfg.n_medusa, cfg.vocab, cfg.d), 0.02, 3002, dev, torch.bfloat16)
+    hh = torch_normal((512, cfg.d), 1.0, 77, dev, torch.bfloat16)
+    idx = torch.empty((512, cfg.n_medusa, 10), dtype=torch.int32, device=dev)
+    val = torch.empty((512, cfg.n_medusa, 10), dtype=torch.float32, device=dev)
+    ws = torch.empty(lib().medusa_heads_topk_workspace_size(1, 512, cfg.d, cfg.vocab, cfg.n_medusa, 10),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        api.medusa_heads_topk(hh, W1, W2, 10, topk_idx=idx, topk_val=val, ws=ws)
+    torch.cuda.synchronize()
+    flop = 2.0 * 512 * cfg.n_medusa * (cfg.d * cfg.d + cfg.vocab * cfg.d)
+    print(json.dumps({"heads_flop": flop, "rows": 512}), flush=True)
 
 
 def attn_traffic_run(dev):
@@ -662,7 +932,7 @@ def tiny_step_rate(dev, steps=16):
     import torch
     from speculative_decoding_heads_amd import api
     from speculative_decoding_heads_amd._lib import GREEDY
-    from speculative_decoding_heads_amd.model import Model, State, prefill, step, step_workspace_size
+    from speculative_decoding_heads_amd.model import Model, State, StepGraph, prefill, step, step_workspace_size
     from workloads import TWO_HEAD_CHOICES, TinyConfig, prompt_tokens, tiny_model
     params, heads = tiny_model(0)
     up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
@@ -672,7 +942,7 @@ def tiny_step_rate(dev, steps=16):
     model = Model(P, {k: up(v) for k, v in heads.items()}, max_pos=512)
     tree = api.Tree(TWO_HEAD_CHOICES)
     prompt = up(prompt_tokens(100, 1, TinyConfig.prompt_len, TinyConfig.vocab).astype(np.int32))
-    st = State(model, 1, 256, 4 * steps)
+    st = State(model, 1, 256, 8 * steps)
     ws = torch.empty(max(1, step_workspace_size(model, tree, 1, 256)), dtype=torch.uint8, device=dev)
     prefill(model, st, prompt)
     for _ in range(3):
@@ -684,8 +954,25 @@ def tiny_step_rate(dev, steps=16):
             step(model, tree, st, GREEDY, L_hint=256, ws=ws)
     us = t.ms() / steps * 1e3
     toks = (int(st.n_out[0]) - n0) / steps
-    return {"us_per_step": round(us, 2), "steps_per_s": round(1e6 / us, 1), "accepted_tokens_per_step": round(toks, 3),
-            "tok_per_s": round(1e6 / us * toks, 1), "bound": "launch latency"}
+    # the same decoding continued by replays of the step captured once (the state advances
+    # with every replay: each replay is the next step)
+    gs = torch.cuda.Stream()
+    g = StepGraph(model, tree, st, GREEDY, L_hint=256, ws=ws, stream=gs)
+    with torch.cuda.stream(gs):
+        g.replay(gs)
+        torch.cuda.synchronize()
+        with Timer() as tg:
+            for _ in range(steps):
+                g.replay(gs)
+        gus = tg.ms() / steps * 1e3
+    torch.cuda.synchronize()
+    assert int(st.err[0]) == 0
+    g.close()
+    best = min(us, gus)
+    return {"us_per_step": round(best, 2), "steps_per_s": round(1e6 / best, 1),
+            "eager_us_per_step": round(us, 2), "graph_us_per_step": round(gus, 2),
+            "accepted_tokens_per_step": round(toks, 3), "tok_per_s": round(1e6 / best * toks, 1),
+            "bound": "launch latency"}
 
 
 def make_gate_up(model, cfg, NL, M, dev):
@@ -718,18 +1005,25 @@ def make_gate_up(model, cfg, NL, M, dev):
     return run
 
 
-def cpu_baseline(params, heads, sample_layers, model, cfg, tree, prompt, prefix, dev):
-    """Oracle (NumPy float64) on a bounded sample of one verify step, scaled to steps/s.
+def cpu_baseline(params, heads, sample_layers, model, cfg, tree, prompt, prefix, dev, gpu):
+    """The oracle on the host cores, timed on bounded samples (median of 3 repetitions).
 
-    Sample: the Medusa heads on one hidden state, two of the 32 decoder layers over the
-    64 tree tokens with a 1024-token prefix, the LM head, and the acceptance rule.  The
-    per-step time is heads + 16 x (two layers) + LM head + acceptance."""
-    import torch
+    Headline (the 7B-shaped verify step): the Medusa heads on one hidden state (one of
+    the 4 heads, scaled x4), 8 of the 32 decoder layers over the 64 tree tokens at the
+    prefix (scaled x4), the LM head and typical acceptance, median of 5; matrix products in float32
+    BLAS, norms, softmax and the rest in float64.  `oracle_by_config` adds the oracle's
+    time for each of the other workloads next to the GPU's (float64 throughout):
+    the tiny fp32 step, the attention at batch 1 / prefix 1024, the heads + top-10 +
+    candidates at batch 1 (one head scaled x4), the attention at batch 8 / prefix 65536
+    (one of its 64 (sequence, KV head) slices, scaled x64) and its compaction."""
+    from oracle.attention import attention_slice, tree_attention as oracle_attention
+    from oracle.candidates import build_candidates
     from oracle.decoder import forward as oracle_forward
     from oracle.heads import medusa_heads_topk
-    from oracle.posterior import TYPICAL, evaluate_posterior_one
+    from oracle.posterior import GREEDY, TYPICAL, evaluate_posterior_one
     from oracle.tree import tree_buffers
-    from workloads import seeded_tree_choices
+    from oracle.update import kv_compact as oracle_compact
+    from workloads import TWO_HEAD_CHOICES, TinyConfig, attention_inputs, seeded_tree_choices, tiny_model
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -742,8 +1036,9 @@ def cpu_baseline(params, heads, sample_layers, model, cfg, tree, prompt, prefix,
              rope_theta=cfg.rope_theta, embed=f32(model.embed), final_norm=f32(model.final_norm),
              lm_head=f32(model.lm_head),
              layers=[{k: f32(v) for k, v in l.items()} for l in sample_layers])
-    W1, W2 = f32(model.W1), f32(model.W2)
-    ot = tree_buffers(seeded_tree_choices(0))
+    W1, W2 = f32(model.W1[:1]), f32(model.W2[:1])
+    H = model.W1.shape[0]
+    ot = tree_buffers(seeded_tree_choices(0), K=10)
     rng = np.random.default_rng(0)
     T = ot["T"]
     Hkv, Dh = cfg.n_kv_heads, cfg.head_dim
@@ -752,31 +1047,80 @@ def cpu_baseline(params, heads, sample_layers, model, cfg, tree, prompt, prefix,
     toks = rng.integers(0, cfg.vocab, (1, T))
     pos = prefix + ot["depth"][None, :]
     h = rng.standard_normal((1, cfg.d)).astype(np.float32)
+    med = lambda xs: float(np.median(xs))
+
+    def timed(f):
+        t0 = time.perf_counter()
+        r = f()
+        return time.perf_counter() - t0, r
+
     log("cpu baseline: timing the oracle")
     per_steps, total = [], 0.0
-    for rep in range(3):
-        t0 = time.perf_counter()
-        medusa_heads_topk(h, W1, W2, 10, bf16=True)
-        t_heads = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        lg, hh, _, _ = oracle_forward(p, toks, pos, Kc, Vc, np.array([prefix]), ot["anc"], bf16=True, layers=nl)
-        t_fwd = time.perf_counter() - t0  # includes the LM head once
-        t0 = time.perf_counter()
-        evaluate_posterior_one(ot, lg[0], toks[0], TYPICAL, 0.7, 0.09, 0.3)
-        t_post = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        _ = hh[0] @ p["lm_head"].astype(np.float64).T
-        t_lm = time.perf_counter() - t0
-        per_steps.append(t_heads + (t_fwd - t_lm) * (cfg.n_layers / nl) + t_lm + t_post)
+    for rep in range(5):
+        t_heads, _ = timed(lambda: medusa_heads_topk(h, W1, W2, 10, bf16=True))
+        t_fwd, (lg, hh, _, _) = timed(lambda: oracle_forward(p, toks, pos, Kc, Vc, np.array([prefix]), ot["anc"],
+                                                             bf16=True, mm_dtype=np.float32, layers=nl))
+        t_post, _ = timed(lambda: evaluate_posterior_one(ot, lg[0], toks[0], TYPICAL, 0.7, 0.09, 0.3))
+        t_lm, _ = timed(lambda: hh[0].astype(np.float32) @ p["lm_head"].T)  # the LM head's share of t_fwd
+        per_steps.append(t_heads * H + (t_fwd - t_lm) * (cfg.n_layers / nl) + t_lm + t_post)
         total += t_heads + t_fwd + t_post + t_lm
         log("cpu baseline rep %d: %.2f s per step" % (rep, per_steps[-1]))
-    per_step = float(np.median(per_steps))
-    log("cpu baseline: %.1f s of oracle work, median %.2f s per step" % (total, per_step))
+    per_step = med(per_steps)
+
+    # ---- the oracle on the other workloads
+    by_cfg = {}
+    tp, th = tiny_model(0)
+    tt = tree_buffers(TWO_HEAD_CHOICES)
+    tK = rng.standard_normal((2, 1, 4, 64, 16))
+    tV = rng.standard_normal((2, 1, 4, 64, 16))
+    ttok = rng.integers(0, TinyConfig.vocab, (1, tt["T"]))
+    tpos = 40 + tt["depth"][None, :]
+    th_in = rng.standard_normal((1, 64))
+
+    def tiny_step():
+        medusa_heads_topk(th_in, th["W1"], th["W2"], tt["K"])
+        lg_, _, _, _ = oracle_forward(tp, ttok, tpos, tK, tV, np.array([40]), tt["anc"])
+        evaluate_posterior_one(tt, lg_[0], ttok[0], GREEDY)
+
+    ts = [timed(tiny_step)[0] for _ in range(3)]
+    by_cfg["tiny_fp32_step"] = {"oracle_us_per_step": round(med(ts) * 1e6, 1), "gpu_us_per_step": gpu["tiny_us"],
+                                "sample": "one step: heads, 2-layer forward over the 9 tree tokens, acceptance"}
+    q, Kc2, Vc2, Kt2, Vt2, seq2 = attention_inputs(3, 1, T, 32, 8, 128, 1024, 1024, bf16=True)
+    ts = [timed(lambda: oracle_attention(q, Kc2, Vc2, seq2, Kt2, Vt2, ot["anc"], 128 ** -0.5))[0] for _ in range(3)]
+    by_cfg["tree_attention_B1_L1024"] = {"oracle_us": round(med(ts) * 1e6, 1), "gpu_us": gpu["attn_b1_us"],
+                                         "sample": "the whole call (32/8 heads x 128, 64-node tree)"}
+    hb = rng.standard_normal((1, cfg.d))
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        tk1, _ = medusa_heads_topk(hb, W1, W2, 10, bf16=True)
+        build_candidates(ot, np.zeros(1, np.int64), np.repeat(tk1, H, axis=1), np.array([prefix]))
+        ts.append((time.perf_counter() - t0) * H)
+    by_cfg["heads_topk_candidates_B1"] = {"oracle_us": round(med(ts) * 1e6, 1), "gpu_us": gpu["heads_b1_us"],
+                                          "sample": "one of the 4 heads (d 4096, V 32000, top-10) scaled x4, "
+                                                    "plus the candidate expansion"}
+    L5 = 65536
+    qs = rng.standard_normal((T, 4, Dh))
+    Ks5 = rng.standard_normal((L5, Dh)).astype(np.float32)
+    Vs5 = rng.standard_normal((L5, Dh)).astype(np.float32)
+    Kt5 = rng.standard_normal((T, Dh))
+    ts = [timed(lambda: attention_slice(qs, Ks5, Vs5, Kt5, Kt5, ot["anc"], 128 ** -0.5))[0] * 64 for _ in range(3)]
+    by_cfg["tree_attention_B8_L65536"] = {"oracle_us": round(med(ts) * 1e6, 1), "gpu_us": gpu["attn_b8_us"],
+                                          "sample": "one (sequence, KV head) slice of the 64, scaled x64"}
+    cK = np.zeros((1, 8, 8, 200, Dh))
+    sK = rng.standard_normal((1, 8, 8, T, Dh))
+    bestc = np.zeros(8, np.int64)
+    accc = np.minimum(np.arange(8) % 5, ot["path_len"][0] - 1)
+    ts = [timed(lambda: oracle_compact(ot, cK, cK, sK, sK, bestc, accc, np.full(8, 100)))[0] for _ in range(3)]
+    by_cfg["kv_compact_B8_1layer"] = {"oracle_us": round(med(ts) * 1e6, 1), "gpu_us": gpu["compact_us"],
+                                      "sample": "the whole call (cache rows beyond 200 do not change the work)"}
+    log("cpu baseline: %.1f s of headline oracle work, median %.2f s per step" % (total, per_step))
     return {"value": round(1.0 / per_step, 5), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": "heads on one hidden state + %d of %d decoder layers over the 64 tree tokens at prefix "
-                      "%d + LM head + typical acceptance, float64 NumPy; per-step time scaled by %d/%d for "
-                      "the layers; median of 3 repetitions (%.1f s measured)" % (nl, cfg.n_layers, prefix,
-                                                                                  cfg.n_layers, nl, total)}
+            "sample": "heads on one hidden state (1 of %d heads, scaled x%d) + %d of %d decoder layers over the 64 "
+                      "tree tokens at prefix %d (scaled x%d) + LM head + typical acceptance; float32 BLAS matrix "
+                      "products, float64 elsewhere; median of 5 repetitions (%.1f s measured)"
+                      % (H, H, nl, cfg.n_layers, prefix, cfg.n_layers // nl, total),
+            "oracle_by_config": by_cfg}
 
 
 if __name__ == "__main__":

@@ -88,6 +88,15 @@ size_t medusa_topk_rows_workspace_size(int M, int V, int K);
 int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* idx, float* val, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/*
+ * Streaming-read ceiling: n_workgroups workgroups each read a contiguous share
+ * of src [bytes] (device, 16-byte aligned, bytes % 16 == 0) with 16-byte loads
+ * and write one word to sink[n_workgroups] (device).  Measures the practical
+ * HBM read rate that the memory-bound kernels are compared with (the page's
+ * roofline remark, section 三, sets their bound by bytes moved).
+ */
+int medusa_read_probe(const void* src, size_t bytes, int n_workgroups, uint32_t* sink, hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Whole model                                                                 */
 /* ------------------------------------------------------------------------- */

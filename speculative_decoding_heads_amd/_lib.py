@@ -33,7 +33,7 @@ EXPORTED = [
     "medusa_step_workspace_size", "medusa_step", "medusa_step_graph_create", "medusa_graph_launch",
     "medusa_graph_destroy", "medusa_step_fused_workspace_size", "medusa_step_fused",
     "medusa_tree_from_acceptance", "medusa_head_hits", "medusa_sample_tokens",
-    "evaluate_posterior_sampled_workspace_size", "evaluate_posterior_sampled",
+    "evaluate_posterior_sampled_workspace_size", "evaluate_posterior_sampled", "medusa_read_probe",
 ]
 
 
@@ -143,6 +143,7 @@ def _declare(lib):
         "evaluate_posterior_sampled_workspace_size": (_S, [_I, _I]),
         "evaluate_posterior_sampled": (_I, [_P, _I, _I, _P, _P, _P, C.POINTER(SamplingDesc), _P, _P, _P, _P, _P, _S,
                                             _P]),
+        "medusa_read_probe": (_I, [_P, _S, _I, _P, _P]),
         "medusa_graph_launch": (_I, [_P, _P]),
         "medusa_graph_destroy": (_I, [_P]),
     }
