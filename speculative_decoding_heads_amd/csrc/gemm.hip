@@ -145,25 +145,47 @@ union F8 {
   bf16x8 v;
 };
 
+// Four bf16 values (round to nearest even) as one 8-byte word, and back.
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  uint2 w;
+  w.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  w.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+  return w;
+}
+__device__ __forceinline__ void unpack_bf16x4(uint2 w, float (&v)[4]) {
+  v[0] = bf16_to_f32((bf16_t)(w.x & 0xffffu));
+  v[1] = bf16_to_f32((bf16_t)(w.x >> 16));
+  v[2] = bf16_to_f32((bf16_t)(w.y & 0xffffu));
+  v[3] = bf16_to_f32((bf16_t)(w.y >> 16));
+}
+
 // Write a wave's (NR*16) x (MB*16) accumulator tile: fp32 partials when the
 // K range is split (layout [batch][SK][M][N]), else the epilogue.  C layout of
-// the 16x16 MFMA: acc[i][j][r] is W row n0 + 16i + 4*lg + r, A row m0 + 16j + l16.
+// the 16x16 MFMA: acc[i][j][r] is W row n0 + 16i + 4*lg + r, A row m0 + 16j + l16,
+// so a lane holds four consecutive outputs of one row: they are written (and a
+// residual read) as one 16-, 8- or 4-byte access when the row stride and base
+// alignment allow, else element by element; the values are the same either way.
 template <int NR, int MB>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[NR][MB], int n0, int m0, int M, int N, int SK, int ks,
                                            int bz, const EpiArgs& e, int64_t sC, int64_t sR, const bf16_t* A,
                                            float* __restrict__ part, int l16, int lg) {
   if (SK > 1 || e.part_only) {
     float* pp = part + (((size_t)bz * SK + ks) * M) * N;
+    const bool vec = (N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
 #pragma unroll
       for (int j = 0; j < MB; ++j) {
         const int m = m0 + j * 16 + l16;
         if (m >= M) continue;
+        const int nb = n0 + i * 16 + 4 * lg;
+        float* dst = pp + (size_t)m * N + nb;
+        if (vec && nb + 3 < N) {
+          *(float4*)dst = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = n0 + i * 16 + 4 * lg + r;
-          if (n < N) pp[(size_t)m * N + n] = acc[i][j][r];
+          for (int r = 0; r < 4; ++r)
+            if (nb + r < N) dst[r] = acc[i][j][r];
         }
       }
     return;
@@ -172,6 +194,20 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[NR][MB], int n0, i
   eb.C = (char*)e.C + bz * sC * (e.mode == MEDUSA_EPI_F32 ? 4 : 2);
   if (e.R) eb.R = (const char*)e.R + bz * sR * 2;
   eb.A = A;
+  const uintptr_t cbase = (uintptr_t)eb.C;
+  bool vec;
+  switch (e.mode) {
+    case MEDUSA_EPI_F32: vec = (e.ldc & 3) == 0 && (cbase & 15) == 0; break;
+    case MEDUSA_EPI_SWIGLU: vec = (e.ldc & 1) == 0 && (cbase & 3) == 0; break;
+    case MEDUSA_EPI_STORE: vec = (e.ldc & 3) == 0 && (cbase & 7) == 0; break;
+    case MEDUSA_EPI_RESID:
+      vec = (e.ldc & 3) == 0 && (cbase & 7) == 0 && (e.ldr & 3) == 0 && ((uintptr_t)eb.R & 7) == 0;
+      break;
+    case MEDUSA_EPI_SILU_RESID_A:
+      vec = (e.ldc & 3) == 0 && (cbase & 7) == 0 && (e.lda & 3) == 0 && ((uintptr_t)A & 7) == 0 && (e.K & 3) == 0;
+      break;
+    default: vec = false; break;
+  }
 #pragma unroll
   for (int i = 0; i < NR; ++i)
 #pragma unroll
@@ -179,13 +215,37 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[NR][MB], int n0, i
       const int m = m0 + j * 16 + l16;
       if (m >= M) continue;
       const int nb = n0 + i * 16 + 4 * lg;
+      const float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       if (e.mode == MEDUSA_EPI_SWIGLU) {
-        if (nb + 1 < N) epi_swiglu<bf16_t>(eb, m, nb / 2, acc[i][j][0], acc[i][j][1]);
-        if (nb + 3 < N) epi_swiglu<bf16_t>(eb, m, nb / 2 + 1, acc[i][j][2], acc[i][j][3]);
+        if (vec && nb + 3 < N) {
+          bf16_t* dst = (bf16_t*)eb.C + (size_t)m * e.ldc + nb / 2;
+          *(uint32_t*)dst = (uint32_t)f32_to_bf16(silu(v[0]) * v[1]) | ((uint32_t)f32_to_bf16(silu(v[2]) * v[3]) << 16);
+        } else {
+          if (nb + 1 < N) epi_swiglu<bf16_t>(eb, m, nb / 2, v[0], v[1]);
+          if (nb + 3 < N) epi_swiglu<bf16_t>(eb, m, nb / 2 + 1, v[2], v[3]);
+        }
+      } else if (vec && nb + 3 < N) {
+        if (e.mode == MEDUSA_EPI_F32) {
+          *(float4*)((float*)eb.C + (size_t)m * e.ldc + nb) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          float o[4] = {v[0], v[1], v[2], v[3]};
+          if (e.mode == MEDUSA_EPI_RESID) {
+            float r[4];
+            unpack_bf16x4(*(const uint2*)((const bf16_t*)eb.R + (size_t)m * e.ldr + nb), r);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = r[q] + o[q];
+          } else if (e.mode == MEDUSA_EPI_SILU_RESID_A) {
+            float r[4];
+            unpack_bf16x4(*(const uint2*)(A + (size_t)m * e.lda + (nb % e.K)), r);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = r[q] + silu(o[q]);
+          }
+          *(uint2*)((bf16_t*)eb.C + (size_t)m * e.ldc + nb) = pack_bf16x4(o[0], o[1], o[2], o[3]);
+        }
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (nb + r < N) epi_store<bf16_t>(eb, m, nb + r, acc[i][j][r]);
+          if (nb + r < N) epi_store<bf16_t>(eb, m, nb + r, v[r]);
       }
     }
 }
@@ -563,14 +623,15 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t off, uint32_t 
                : "memory", "m0");
 }
 
-// Streaming kernel for every M (K % 64 == 0) with a deep ring of LDS chunk buffers.  Same
+// Streaming kernel for every M (K % 64 == 0) with a ring of LDS chunk buffers.  Same
 // tile ownership and accumulator layout as gemm_lds_kernel (NWV waves, each
 // NR*16 W rows, 64 A rows, 16x16x32 products), but both operands travel
-// global -> LDS by 16-byte direct loads, so the depth of the pipeline is set
-// by the 160 KB of LDS rather than by registers: D chunks of 64 k (one
-// 128-byte line of every W and A row) are in the ring, D - 1 of them in
-// flight.  A product of this shape streams its weights once, and its rate
-// follows the bytes each CU keeps in flight.  Each wave loads its own W rows;
+// global -> LDS by 16-byte direct loads: D chunks of 64 k (one 128-byte line
+// of every W and A row) are in the ring, D - 1 of them in flight.  A product
+// of this shape streams its weights once.  A CU's streaming rate stops growing
+// once 2-3 chunks (about 40-70 KB) are in flight, while a deeper ring delays
+// the first chunk (every workgroup's whole fill is queued at once), so the ring
+// is 3-4 chunks deep rather than as deep as the LDS allows.  Each wave loads its own W rows;
 // the 64 A rows of a chunk are split over the waves; one barrier per chunk
 // makes the chunk visible and frees the buffer read in the previous step.  The
 // 16-byte pieces of a row are permuted by (row / 2) mod 8 so the fragment reads
@@ -863,24 +924,28 @@ void gemm_bf16_launch(const GemmPlan& p0, int M, int N, int K, const void* A, in
 #define GEMM_LAUNCH_DMA(NRV, NWVV, DV)                                                                       \
   hipLaunchKernelGGL((gemm_dma_kernel<NRV, NWVV, DV>), grid, dim3(NWVV * 64), 0, stream, M, N, K,               \
                      (const bf16_t*)A, lda, strideA, (const bf16_t*)W, strideW, p.SK, e, strideC, strideR, (float*)ws)
-  static const int e_half = env_int("MEDUSA_GEMM_DMA_HALF", 0);  // tuning runs: a ring of about half the depth
-  if (p.LDS && p.DMA && e_half) {
-    if (p.NR == 1) {
-      if (p.NWV == 3) GEMM_LAUNCH_DMA(1, 3, 6);
-      else GEMM_LAUNCH_DMA(1, 4, 5);
-    } else {
-      if (p.NWV == 3) GEMM_LAUNCH_DMA(2, 3, 4);
-      else GEMM_LAUNCH_DMA(2, 4, 4);
-    }
-  } else if (p.LDS && p.DMA) {
-    // ring depth: as many 64-k chunks as fit the LDS
-    if (p.NR == 1) {
-      if (p.NWV == 3) GEMM_LAUNCH_DMA(1, 3, 11);
-      else GEMM_LAUNCH_DMA(1, 4, 9);
-    } else {
-      if (p.NWV == 3) GEMM_LAUNCH_DMA(2, 3, 7);
-      else GEMM_LAUNCH_DMA(2, 4, 6);
-    }
+  // ring depth (64-k chunks): MEDUSA_GEMM_DMA_D = 3..6 overrides it for tuning runs
+  static const int e_depth = env_int("MEDUSA_GEMM_DMA_D", 0);
+  if (p.LDS && p.DMA) {
+    const int kind = (p.NR - 1) * 2 + (p.NWV == 4 ? 1 : 0);
+    // Measured on the 64-row projections and the 1-row heads: the first chunk
+    // of a deep ring waits behind every workgroup's whole ring fill (about
+    // 3.2 us for 10 chunks in flight, 1.9 us for 3), while the streaming rate
+    // stays the same from 2-3 chunks in flight per CU on.
+    static const int dflt[4] = {4, 4, 4, 3};  // (NR, waves) = (1, 3), (1, 4), (2, 3), (2, 4)
+    const int dd = e_depth >= 3 && e_depth <= 6 ? e_depth : dflt[kind];
+#define DMA_DEPTHS(NRV, NWVV)                    \
+  do {                                           \
+    if (dd == 3) GEMM_LAUNCH_DMA(NRV, NWVV, 3);  \
+    else if (dd == 4) GEMM_LAUNCH_DMA(NRV, NWVV, 4); \
+    else if (dd == 5) GEMM_LAUNCH_DMA(NRV, NWVV, 5); \
+    else GEMM_LAUNCH_DMA(NRV, NWVV, 6);          \
+  } while (0)
+    if (kind == 0) DMA_DEPTHS(1, 3);
+    else if (kind == 1) DMA_DEPTHS(1, 4);
+    else if (kind == 2) DMA_DEPTHS(2, 3);
+    else DMA_DEPTHS(2, 4);
+#undef DMA_DEPTHS
   } else if (p.LDS) {
     if (p.NWV == 3 && p.NR == 1) {
       if (p.U == 2) GEMM_LAUNCH_LDS(1, 2, 4, 3);

@@ -48,6 +48,7 @@ def _run(dev, choices, B, Hq, Hkv, Dh, L, Lmax, dtype_name, seed, ragged=False, 
     (TWO_HEAD_CHOICES, 2, 32, 2, 333, 384, True),        # G = 16: 144 rows -> a partial 32-row block
     (chain_choices(11), 1, 32, 2, 2000, 2048, False),    # G = 16: 192 rows, a chain tree
     (seeded_tree_choices(0), 1, 32, 32, 1024, 1088, False),  # MHA 64 rows (7B shape)
+    (seeded_tree_choices(0), 2, 32, 8, 1024, 1024, True),  # split KV over ragged 1k prefixes
 ])
 def test_bf16_mfma_parity(dev, choices, B, Hq, Hkv, L, Lmax, ragged):
     got, ref = _run(dev, choices, B, Hq, Hkv, 128, L, Lmax, "bf16", seed=L + B, ragged=ragged)
