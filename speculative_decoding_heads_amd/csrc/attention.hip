@@ -147,13 +147,11 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
     l1 = ws_ml[(base + (size_t)(lane + 32) * R) * 2 + 1];
   }
   float mt = fmaxf(m0, m1);
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 32));
+  butterfly<5>([&](auto S) { mt = fmaxf(mt, bfly<decltype(S)::value>(mt)); });  // within the half wave
   const float w0 = m0 != -INFINITY ? __builtin_amdgcn_exp2f(m0 - mt) : 0.f;
   const float w1 = m1 != -INFINITY ? __builtin_amdgcn_exp2f(m1 - mt) : 0.f;
   float lt = l0 * w0 + l1 * w1;
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) lt += __shfl_xor(lt, o, 32);
+  butterfly<5>([&](auto S) { lt += bfly<decltype(S)::value>(lt); });
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

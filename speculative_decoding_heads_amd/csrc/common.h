@@ -1,5 +1,6 @@
 // Shared helpers of the libmedusa kernels and host entry points (gfx950 only).
 #pragma once
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,14 +59,58 @@ template <> struct Elem<bf16_t> {
 inline size_t dtype_size(int dtype) { return dtype == MEDUSA_BF16 ? 2 : 4; }
 inline bool dtype_ok(int dtype) { return dtype == MEDUSA_F32 || dtype == MEDUSA_BF16; }
 
+// Cross-lane butterfly without LDS: at step S a lane reads the value of its
+// partner, which reads the lane's in turn.  Steps 0-3 are DPP permutations
+// inside each row of 16 lanes (neighbours, pairs, mirror within 8, mirror
+// within 16), step 4 pairs rows r and r ^ 1 and step 5 the two halves (the
+// gfx950 v_permlane16/32_swap, which with both operands the same register
+// return the lane's own value and its partner's).  Steps 0..4 combine the 32
+// lanes of a half wave, 0..5 the whole wave; because partners are mutual, a
+// commutative merge leaves the same result in every lane.
+__device__ __forceinline__ unsigned lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+template <int S>
+__device__ __forceinline__ unsigned bfly_u32(unsigned x) {
+  if constexpr (S == 0) return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 1) return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S == 2) return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);
+  else if constexpr (S == 3) return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false);
+  else if constexpr (S == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane_id() & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane_id() & 32) ? r[0] : r[1];
+  }
+}
+template <int S>
+__device__ __forceinline__ float bfly(float x) {
+  return __uint_as_float(bfly_u32<S>(__float_as_uint(x)));
+}
+template <int S>
+__device__ __forceinline__ int bfly(int x) {
+  return (int)bfly_u32<S>((unsigned)x);
+}
+// f(std::integral_constant<int, S>{}) for S = 0 .. NSTEP-1 (6: a wave, 5: a half wave)
+template <int NSTEP = 6, class F>
+__device__ __forceinline__ void butterfly(F&& f) {
+  f(std::integral_constant<int, 0>{});
+  f(std::integral_constant<int, 1>{});
+  f(std::integral_constant<int, 2>{});
+  f(std::integral_constant<int, 3>{});
+  f(std::integral_constant<int, 4>{});
+  if constexpr (NSTEP > 5) f(std::integral_constant<int, 5>{});
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  butterfly([&](auto S) { v = fmaxf(v, bfly<decltype(S)::value>(v)); });
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  butterfly([&](auto S) { v += bfly<decltype(S)::value>(v); });
+  return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+  butterfly([&](auto S) { v = max(v, bfly<decltype(S)::value>(v)); });
   return v;
 }
 

@@ -103,15 +103,15 @@ __global__ __launch_bounds__(256) void argmax_rows_kernel(int V, const float* __
   }
   __shared__ float sv[4];
   __shared__ int si[4];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(bv, o, 64);
-    const int i2 = __shfl_xor(bi, o, 64);
+  butterfly([&](auto S) {
+    constexpr int s = decltype(S)::value;
+    const float v2 = bfly<s>(bv);
+    const int i2 = bfly<s>(bi);
     if (v2 > bv || (v2 == bv && i2 < bi)) {
       bv = v2;
       bi = i2;
     }
-  }
+  });
   if ((threadIdx.x & 63) == 0) {
     sv[threadIdx.x >> 6] = bv;
     si[threadIdx.x >> 6] = bi;

@@ -7,10 +7,15 @@
 //   1. z = h + SiLU(W1 h) for all heads at once (W1 stacked [H*d, d]) with the
 //      residual fused into the product's epilogue, z stored in the input dtype;
 //   2. logits[b, k, :] = W2[k] z[b, k] as H batched products (fp32 out);
-//   3. top-K per (b, k) row in two stages: one wave per vocabulary chunk keeps
-//      a sorted per-lane register list, then K rounds of a wave-wide
-//      (value desc, index asc) maximum pop the chunk's K best; one wave per row
-//      merges the chunks' candidates the same way.
+//   3. top-K per (b, k) row: for up to 768 rows of at most 32768 entries, one
+//      1024-thread workgroup per row (threshold from the thread maxima, the few
+//      entries above it compacted in LDS, K selection rounds over them); else
+//      in two stages: one wave per vocabulary chunk keeps a sorted per-lane
+//      register list, then K rounds of a wave-wide (value desc, index asc)
+//      maximum pop the chunk's K best; one wave per row merges the chunks'
+//      candidates the same way.
+#include <stdlib.h>
+
 #include "common.h"
 #include "medusa_model.h"
 
@@ -23,6 +28,44 @@ constexpr int TK_PER_LANE = 8;  // vocabulary entries per lane in the first stag
 
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Best (value desc, index asc) pair of a wave, in every lane, without LDS:
+// DPP permutations inside each row of 16 lanes (swap neighbours, swap pairs,
+// mirror within 8, mirror within 16), then the gfx950 row swaps (rows r and
+// r ^ 1, then halves) -- each step pairs every lane with one not yet merged.
+// The order is total on non-NaN values, so any merge tree gives the same pair.
+template <int CTRL>
+__device__ __forceinline__ void best_dpp(float& bv, int& bi) {
+  const float v2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int i2 = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
+  if (better(v2, i2, bv, bi)) {
+    bv = v2;
+    bi = i2;
+  }
+}
+// r[0], r[1] of a row swap with both operands the same register are the lane's
+// own value and its partner's, in some order
+__device__ __forceinline__ void best_of_swap(float& bv, int& bi, const __attribute__((ext_vector_type(2))) unsigned rv,
+                                             const __attribute__((ext_vector_type(2))) unsigned ri) {
+  bv = __uint_as_float(rv[0]);
+  bi = (int)ri[0];
+  const float v2 = __uint_as_float(rv[1]);
+  const int i2 = (int)ri[1];
+  if (better(v2, i2, bv, bi)) {
+    bv = v2;
+    bi = i2;
+  }
+}
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+  best_dpp<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
+  best_dpp<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
+  best_dpp<0x141>(bv, bi);  // row_half_mirror
+  best_dpp<0x140>(bv, bi);  // row_mirror
+  best_of_swap(bv, bi, __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false),
+               __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false));
+  best_of_swap(bv, bi, __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false),
+               __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false));
 }
 
 // Per-lane sorted list (best first) of up to TK_MAX candidates.
@@ -57,15 +100,7 @@ struct LaneList {
     for (int r = 0; r < K; ++r) {
       float bv = v[0];
       int bi = i[0];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float v2 = __shfl_xor(bv, o, 64);
-        const int i2 = __shfl_xor(bi, o, 64);
-        if (better(v2, i2, bv, bi)) {
-          bv = v2;
-          bi = i2;
-        }
-      }
+      wave_best(bv, bi);
       if (threadIdx.x == 0) {
         out_v[r] = bv;
         out_i[r] = bi;
@@ -128,15 +163,7 @@ __global__ __launch_bounds__(64) void topk_stage1_kernel(int V, int chunk, const
     for (int rd = 0; rd < K; ++rd) {
       float bv = v;
       int bl = lane;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float v2 = __shfl_xor(bv, o, 64);
-        const int l2 = __shfl_xor(bl, o, 64);
-        if (v2 > bv || (v2 == bv && l2 < bl)) {
-          bv = v2;
-          bl = l2;
-        }
-      }
+      wave_best(bv, bl);
       t = bv;
       if (lane == bl) v = -INFINITY;
     }
@@ -166,6 +193,180 @@ __global__ __launch_bounds__(64) void topk_stage2_kernel(int ncand, const float*
     const int t = si[threadIdx.x];
     idx[(size_t)row * K + threadIdx.x] = t == 0x7fffffff ? 0 : t;
     if (val) val[(size_t)row * K + threadIdx.x] = sv[threadIdx.x];
+  }
+}
+
+// One workgroup of 1024 threads per row (rows of at most 8 * 4096 entries):
+// the whole row sits in registers (NV float4 batches a thread) and the top K
+// come out of three steps with no second launch.
+//  1. t = the K-th largest of the 1024 thread maxima (each wave's K largest
+//     lane maxima into LDS, then every wave ranks the 16 * K of them).  The K
+//     threads behind those maxima hold K distinct entries >= t, so the row's
+//     K-th largest entry is >= t.
+//  2. Every entry >= t is appended to an LDS list (typically a few dozen).
+//  3. One wave takes K rounds of a (value desc, index asc) maximum over the
+//     list, each round over the entries strictly after the previous winner.
+// If more than TR_CAP entries reach t (a plateau of equal values), step 3 runs
+// over every thread's registers instead, with a block-wide maximum per round.
+// Either way the result is the exact top K in that order.
+constexpr int TR_THREADS = 1024;
+constexpr int TR_WAVES = TR_THREADS / 64;
+constexpr int TR_CAP = 2048;
+constexpr int TR_MAX_NV = 8;  // rows up to 8 * 4 * 1024 = 32768 entries (longer rows spill registers)
+
+template <int NV>
+__global__ __launch_bounds__(TR_THREADS) void topk_row_kernel(int V, const float* __restrict__ x, int K, int vec,
+                                                              int32_t* __restrict__ idx, float* __restrict__ val) {
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* r = x + (size_t)row * V;
+  __shared__ float s_wk[TR_WAVES * TK_MAX];
+  __shared__ float s_cv[TR_CAP];
+  __shared__ int s_ci[TR_CAP];
+  __shared__ float s_rv[2][TR_WAVES];
+  __shared__ int s_ri[2][TR_WAVES];
+  __shared__ int s_cnt;
+  // element e = 4u + c of this thread: index (u * 1024 + tid) * 4 + c (float4
+  // batches) or (4u + c) * 1024 + tid (scalar loads)
+  auto index_of = [&](int u, int c) __attribute__((always_inline)) {
+    return vec ? (u * TR_THREADS + tid) * 4 + c : (4 * u + c) * TR_THREADS + tid;
+  };
+  float v[NV * 4];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    if (vec && (u * TR_THREADS + tid) * 4 + 3 < V) {
+      const float4 b = *(const float4*)(r + (u * TR_THREADS + tid) * 4);
+      v[4 * u] = b.x;
+      v[4 * u + 1] = b.y;
+      v[4 * u + 2] = b.z;
+      v[4 * u + 3] = b.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int k = index_of(u, c);
+        v[4 * u + c] = k < V ? r[k] : -INFINITY;
+      }
+    }
+  }
+  if (tid == 0) s_cnt = 0;
+  // 1. threshold
+  float tm = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < NV * 4; ++e) tm = fmaxf(tm, v[e]);
+  {
+    float cur = tm;
+    for (int rd = 0; rd < K; ++rd) {
+      float bv = cur;
+      int bl = lane;
+      wave_best(bv, bl);  // lowest lane on ties: a lane index works as the tie-break key
+      if (lane == 0) s_wk[w * TK_MAX + rd] = bv;
+      if (lane == bl) cur = -INFINITY;
+    }
+  }
+  __syncthreads();
+  float t;
+  {
+    // every wave ranks the TR_WAVES * K maxima (at most 4 a lane)
+    float c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = lane + 64 * q;
+      c[q] = j < TR_WAVES * K ? s_wk[(j / K) * TK_MAX + j % K] : -INFINITY;
+    }
+    t = -INFINITY;
+    for (int rd = 0; rd < K; ++rd) {
+      float bv = c[0];
+      int bq = 0;
+#pragma unroll
+      for (int q = 1; q < 4; ++q)
+        if (c[q] > bv) {
+          bv = c[q];
+          bq = q;
+        }
+      int bl = lane * 4 + bq;
+      wave_best(bv, bl);
+      t = bv;
+      if (lane == bl / 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q == bl % 4) c[q] = -INFINITY;
+      }
+    }
+  }
+  // 2. entries >= t into the LDS list
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = index_of(u, c);
+      if (k < V && v[4 * u + c] >= t) {
+        const int p = atomicAdd(&s_cnt, 1);
+        if (p < TR_CAP) {
+          s_cv[p] = v[4 * u + c];
+          s_ci[p] = k;
+        }
+      }
+    }
+  __syncthreads();
+  const int n = s_cnt;
+  // 3. K rounds, each over the entries strictly after the previous winner
+  float pv = INFINITY;
+  int pi = -1;
+  if (n <= TR_CAP) {
+    if (w != 0) return;
+    for (int rd = 0; rd < K; ++rd) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int j = lane; j < n; j += 64) {
+        const float cv = s_cv[j];
+        const int ci = s_ci[j];
+        if (better(pv, pi, cv, ci) && better(cv, ci, bv, bi)) {
+          bv = cv;
+          bi = ci;
+        }
+      }
+      wave_best(bv, bi);
+      if (lane == 0) {
+        idx[(size_t)row * K + rd] = bi == 0x7fffffff ? 0 : bi;
+        if (val) val[(size_t)row * K + rd] = bv;
+      }
+      pv = bv;
+      pi = bi;
+    }
+    return;
+  }
+  for (int rd = 0; rd < K; ++rd) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int k = index_of(u, c);
+        const float cv = v[4 * u + c];
+        if (k < V && better(pv, pi, cv, k) && better(cv, k, bv, bi)) {
+          bv = cv;
+          bi = k;
+        }
+      }
+    wave_best(bv, bi);
+    if (lane == 0) {
+      s_rv[rd & 1][w] = bv;
+      s_ri[rd & 1][w] = bi;
+    }
+    __syncthreads();
+    bv = s_rv[rd & 1][0];
+    bi = s_ri[rd & 1][0];
+    for (int j = 1; j < TR_WAVES; ++j)
+      if (better(s_rv[rd & 1][j], s_ri[rd & 1][j], bv, bi)) {
+        bv = s_rv[rd & 1][j];
+        bi = s_ri[rd & 1][j];
+      }
+    if (tid == 0) {
+      idx[(size_t)row * K + rd] = bi == 0x7fffffff ? 0 : bi;
+      if (val) val[(size_t)row * K + rd] = bv;
+    }
+    pv = bv;
+    pi = bi;
   }
 }
 
@@ -216,6 +417,26 @@ extern "C" int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* id
   MEDUSA_REQUIRE(x && idx, MEDUSA_ERR_ARG, "topk_rows: null pointer");
   MEDUSA_REQUIRE(ws && ws_bytes >= topk_ws(M, V, K), MEDUSA_ERR_WORKSPACE, "topk_rows: workspace %zu < %zu", ws_bytes,
                  topk_ws(M, V, K));
+  const int vec4 = V % 4 == 0 && ((uintptr_t)x & 15) == 0;
+  const int nv = (V + 4 * TR_THREADS - 1) / (4 * TR_THREADS);
+  // One workgroup per row reads a row at one CU's rate, so with many rows the
+  // two-stage path (each row spread over many waves) wins: measured at V 32000,
+  // 17 vs 26 us at 4 rows, 38 vs 46 us at 512, 127 vs 99 us at 2048.
+  // MEDUSA_TOPK_ROW_MAX_M overrides the 768-row limit (tuning runs).
+  static const int e_rows = [] {
+    const char* e = getenv("MEDUSA_TOPK_ROW_MAX_M");
+    return e ? atoi(e) : 768;
+  }();
+  if (nv <= TR_MAX_NV && M <= e_rows) {
+#define TR_LAUNCH(NVV) \
+  hipLaunchKernelGGL(topk_row_kernel<NVV>, dim3(M), dim3(TR_THREADS), 0, stream, V, x, K, vec4, idx, val)
+    if (nv <= 1) TR_LAUNCH(1);
+    else if (nv <= 2) TR_LAUNCH(2);
+    else if (nv <= 4) TR_LAUNCH(4);
+    else TR_LAUNCH(8);
+#undef TR_LAUNCH
+    return check_launch("topk_rows");
+  }
   const int nch = topk_chunks(M, V);
   int chunk = (V + nch - 1) / nch;
   const int vec = V % 4 == 0 && ((uintptr_t)x & 15) == 0;

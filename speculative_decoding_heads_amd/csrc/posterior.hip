@@ -80,13 +80,10 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
       z = z * __builtin_amdgcn_exp2f((bv - m) * c2) + z2 * __builtin_amdgcn_exp2f((v2 - m) * c2);
     argmax_merge(bv, bi, v2, i2);
   };
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(bv, o, 64);
-    const int i2 = __shfl_xor(bi, o, 64);
-    const float z2 = __shfl_xor(z, o, 64);
-    merge(v2, i2, z2);
-  }
+  butterfly([&](auto S) {
+    constexpr int s = decltype(S)::value;
+    merge(bfly<s>(bv), bfly<s>(bi), bfly<s>(z));
+  });
   if (lane == 0) {
     s_v[w] = bv;
     s_i[w] = bi;
@@ -172,8 +169,7 @@ __global__ __launch_bounds__(64) void select_kernel(const medusa_tree_host* __re
   }
   // a = max acc
   int a = acc;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) a = max(a, __shfl_xor(a, o, 64));
+  a = wave_max_int(a);
   int best = 0;
   if (a > 0) {
     const bool cand = acc == a;
@@ -182,8 +178,7 @@ __global__ __launch_bounds__(64) void select_kernel(const medusa_tree_host* __re
       best = __ffsll((unsigned long long)m) - 1;
     } else {
       float l = cand ? lik : -INFINITY;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) l = fmaxf(l, __shfl_xor(l, o, 64));
+      l = wave_max(l);
       const uint64_t m = __ballot(cand && lik == l);
       best = __ffsll((unsigned long long)m) - 1;
     }

@@ -124,8 +124,10 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
       bi = i2;
     }
   };
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) merge(__shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64), __shfl_xor(z, o, 64));
+  butterfly([&](auto S) {
+    constexpr int s = decltype(S)::value;
+    merge(bfly<s>(bv), bfly<s>(bi), bfly<s>(z));
+  });
   if (lane == 0) {
     s_v[w] = bv;
     s_i[w] = bi;
@@ -222,15 +224,15 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
       if (k + 3 < V) take(x[k + 3], k + 3, r.w);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float s2 = __shfl_xor(bs, o, 64);
-    const int t2 = __shfl_xor(bt, o, 64);
+  butterfly([&](auto S) {
+    constexpr int s = decltype(S)::value;
+    const float s2 = bfly<s>(bs);
+    const int t2 = bfly<s>(bt);
     if (score_better(s2, t2, bs, bt)) {
       bs = s2;
       bt = t2;
     }
-  }
+  });
   __syncthreads();
   if (lane == 0) {
     s_v[w] = bs;
@@ -271,8 +273,7 @@ __global__ __launch_bounds__(64) void select_match_kernel(const medusa_tree_host
     }
   }
   int amax = acc;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = max(amax, __shfl_xor(amax, o, 64));
+  amax = wave_max_int(amax);
   int best = 0;
   if (amax > 0) {
     const uint64_t msk = __ballot(acc == amax);
