@@ -116,6 +116,11 @@ __device__ __forceinline__ int wave_max_int(int v) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Embedding rows of tokens into x and their RMSNorm (weight w) into y in one
+// launch; the same values as medusa_embed then medusa_rmsnorm (elementwise.hip).
+int embed_rmsnorm(int dtype, int M, int d, const int32_t* tokens, const void* table, int V, const void* w, float eps,
+                  void* x, void* y, hipStream_t stream);
+
 // bf16 RMSNorm of M rows of length N (N % 8 == 0, N <= 8192, 16-byte aligned
 // rows), optionally after adding SK fp32 split-K partials [SK][M][N] into x
 // (gemm.hip).

@@ -79,6 +79,37 @@ __global__ void embed_kernel(int d, const int32_t* __restrict__ tok, const T* __
   for (int n = threadIdx.x; n < d; n += blockDim.x) out[(size_t)m * d + n] = table[(size_t)v * d + n];
 }
 
+// Embedding gather fused with the first layer's input RMSNorm: one block per
+// row writes the gathered row to x and its norm to y, with the same per-thread
+// element assignment, summation order and formula as rmsnorm_kernel (so y
+// equals medusa_embed followed by medusa_rmsnorm bit for bit).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_rmsnorm_kernel(int d, const int32_t* __restrict__ tok,
+                                                            const T* __restrict__ table, int V,
+                                                            const T* __restrict__ w, float eps, T* __restrict__ x,
+                                                            T* __restrict__ y) {
+  const int m = blockIdx.x;
+  int v = tok[m];
+  v = v < 0 ? 0 : (v >= V ? V - 1 : v);
+  const T* src = table + (size_t)v * d;
+  T* xr = x + (size_t)m * d;
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int n = threadIdx.x; n < d; n += 256) {
+    const T e = src[n];
+    xr[n] = e;
+    const float f = Elem<T>::load(&e, 0);
+    ss += f * f;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int n = threadIdx.x; n < d; n += 256)
+    Elem<T>::store(y, (size_t)m * d + n, Elem<T>::load(src, n) * inv * Elem<T>::load(w, n));
+}
+
 template <typename T>
 __global__ void gather_rows_kernel(int T_, int d, const T* __restrict__ h, const int32_t* __restrict__ sel,
                                    T* __restrict__ out) {
@@ -180,6 +211,25 @@ extern "C" int medusa_embed(int dtype, int M, int d, const int32_t* tokens, cons
                        (bf16_t*)out);
   return check_launch("embed");
 }
+
+namespace medusa {
+
+int embed_rmsnorm(int dtype, int M, int d, const int32_t* tokens, const void* table, int V, const void* w, float eps,
+                  void* x, void* y, hipStream_t stream) {
+  MEDUSA_REQUIRE(dtype_ok(dtype), MEDUSA_ERR_UNSUPPORTED, "embed_rmsnorm: dtype");
+  MEDUSA_REQUIRE(M >= 0 && d > 0 && V > 0, MEDUSA_ERR_ARG, "embed_rmsnorm: bad sizes");
+  if (M == 0) return MEDUSA_OK;
+  MEDUSA_REQUIRE(tokens && table && w && x && y, MEDUSA_ERR_ARG, "embed_rmsnorm: null pointer");
+  if (dtype == MEDUSA_F32)
+    hipLaunchKernelGGL(embed_rmsnorm_kernel<float>, dim3(M), dim3(256), 0, stream, d, tokens, (const float*)table, V,
+                       (const float*)w, eps, (float*)x, (float*)y);
+  else
+    hipLaunchKernelGGL(embed_rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, d, tokens, (const bf16_t*)table,
+                       V, (const bf16_t*)w, eps, (bf16_t*)x, (bf16_t*)y);
+  return check_launch("embed_rmsnorm");
+}
+
+}  // namespace medusa
 
 extern "C" int medusa_gather_rows(int dtype, int B, int T, int d, const void* h, const int32_t* sel, void* out,
                                   hipStream_t stream) {

@@ -161,11 +161,11 @@ int forward_impl(const medusa_model* m, int B, int T, const int32_t* tokens, con
   };
   const medusa_trace none = {};
   const medusa_trace& t = tr ? *tr : none;
-  CK(medusa_embed(dt, M, d, tokens, m->embed, m->vocab, f.x, stream));
+  // the embedding gather also applies the first layer's input RMSNorm, and each
+  // residual projection the RMSNorm that feeds the next sub-layer (the last one
+  // the final norm, into h)
+  CK(embed_rmsnorm(dt, M, d, tokens, m->embed, m->vocab, m->layers[0].attn_norm, m->norm_eps, f.x, f.xn, stream));
   CK(trace(t.x, 0, f.x, d));
-  // each residual projection also applies the RMSNorm that feeds the next
-  // sub-layer (the last one the final norm, into h)
-  CK(medusa_rmsnorm(dt, M, d, f.x, m->layers[0].attn_norm, m->norm_eps, f.xn, stream));
   for (int l = 0; l < m->n_layers; ++l) {
     const medusa_layer_weights& w = m->layers[l];
     const bool last = l + 1 == m->n_layers;
