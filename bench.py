@@ -90,7 +90,9 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--attn-reps", type=int, default=20)
-    p.add_argument("--roofline-only", action="store_true")
+    p.add_argument("--roofline-only", action="store_true",
+                   help="for rocprofv3 --pmc: the gate/up projection over the 32 layers' weights, a 256 MiB row copy "
+                        "and 1 GiB streaming reads at 256 and 2048 workgroups")
     p.add_argument("--attn-traffic-only", action="store_true")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     p.add_argument("--heads-only", action="store_true")
@@ -362,6 +364,14 @@ def main():
         sel = torch.zeros(rows, dtype=torch.int32, device=dev)
         for _ in range(3):
             check(lib().medusa_gather_rows(0, rows, 1, 2048, ptr(src), ptr(sel), ptr(dst), stream_ptr()))
+        del src, dst
+        # plain streaming reads of 1 GiB beside it (for latency counters): one
+        # workgroup per CU, then eight
+        rp = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty(2048, dtype=torch.int32, device=dev)
+        for nwg in (256, 2048):
+            for _ in range(3):
+                check(lib().medusa_read_probe(ptr(rp), rp.numel() * 4, nwg, ptr(sink), stream_ptr()))
         torch.cuda.synchronize()
         print(json.dumps({"gate_up_us": round(us, 3), "copy_bytes": COPY_BYTES}), flush=True)
         return

@@ -117,7 +117,8 @@ __device__ __forceinline__ int wave_max_int(int v) {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Embedding rows of tokens into x and their RMSNorm (weight w) into y in one
-// launch; the same values as medusa_embed then medusa_rmsnorm (elementwise.hip).
+// launch; x as medusa_embed writes it, y by medusa_rmsnorm's formula
+// (elementwise.hip).
 int embed_rmsnorm(int dtype, int M, int d, const int32_t* tokens, const void* table, int V, const void* w, float eps,
                   void* x, void* y, hipStream_t stream);
 

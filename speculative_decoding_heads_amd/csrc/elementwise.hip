@@ -79,11 +79,12 @@ __global__ void embed_kernel(int d, const int32_t* __restrict__ tok, const T* __
   for (int n = threadIdx.x; n < d; n += blockDim.x) out[(size_t)m * d + n] = table[(size_t)v * d + n];
 }
 
-// Embedding gather fused with the first layer's input RMSNorm: one block per
-// row writes the gathered row to x and its norm to y, with the same per-thread
-// element assignment, summation order and formula as rmsnorm_kernel (so y
-// equals medusa_embed followed by medusa_rmsnorm bit for bit).
-template <typename T>
+// Embedding gather fused with the first layer's input RMSNorm: one 256-thread
+// block per row; with bf16 rows of d % 8 == 0 and d <= 8192 each thread keeps
+// NV 16-byte pieces of the row in registers (one read of the table row), else
+// element by element.  y = x * inv * w with inv = 1 / sqrt(mean(x^2) + eps),
+// the formula of rmsnorm_kernel (the sum is taken in a different order).
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void embed_rmsnorm_kernel(int d, const int32_t* __restrict__ tok,
                                                             const T* __restrict__ table, int V,
                                                             const T* __restrict__ w, float eps, T* __restrict__ x,
@@ -93,21 +94,63 @@ __global__ __launch_bounds__(256) void embed_rmsnorm_kernel(int d, const int32_t
   v = v < 0 ? 0 : (v >= V ? V - 1 : v);
   const T* src = table + (size_t)v * d;
   T* xr = x + (size_t)m * d;
+  T* yr = y + (size_t)m * d;
   __shared__ float red[4];
   float ss = 0.f;
-  for (int n = threadIdx.x; n < d; n += 256) {
-    const T e = src[n];
-    xr[n] = e;
-    const float f = Elem<T>::load(&e, 0);
-    ss += f * f;
+  if constexpr (NV > 0) {
+    // piece j of this thread: elements (j * 256 + tid) * 8 .. + 8
+    uint4 raw[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e0 = (j * 256 + (int)threadIdx.x) * 8;
+      if (e0 < d) {
+        raw[j] = *(const uint4*)(src + e0);
+        *(uint4*)(xr + e0) = raw[j];
+        const uint32_t* u = (const uint32_t*)&raw[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_to_f32((bf16_t)(u[q] & 0xffffu)), hi = bf16_to_f32((bf16_t)(u[q] >> 16));
+          ss += lo * lo + hi * hi;
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e0 = (j * 256 + (int)threadIdx.x) * 8;
+      if (e0 < d) {
+        const uint4 wr = *(const uint4*)(w + e0);
+        const uint32_t* u = (const uint32_t*)&raw[j];
+        const uint32_t* g = (const uint32_t*)&wr;
+        uint4 out;
+        uint32_t* o = (uint32_t*)&out;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a0 = bf16_to_f32((bf16_t)(u[q] & 0xffffu)) * inv * bf16_to_f32((bf16_t)(g[q] & 0xffffu));
+          const float a1 = bf16_to_f32((bf16_t)(u[q] >> 16)) * inv * bf16_to_f32((bf16_t)(g[q] >> 16));
+          o[q] = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
+        }
+        *(uint4*)(yr + e0) = out;
+      }
+    }
+  } else {
+    for (int n = threadIdx.x; n < d; n += 256) {
+      const T e = src[n];
+      xr[n] = e;
+      const float f = Elem<T>::load(&e, 0);
+      ss += f * f;
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+    for (int n = threadIdx.x; n < d; n += 256) Elem<T>::store(yr, n, Elem<T>::load(src, n) * inv * Elem<T>::load(w, n));
   }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
-  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int n = threadIdx.x; n < d; n += 256)
-    Elem<T>::store(y, (size_t)m * d + n, Elem<T>::load(src, n) * inv * Elem<T>::load(w, n));
 }
 
 template <typename T>
@@ -220,12 +263,24 @@ int embed_rmsnorm(int dtype, int M, int d, const int32_t* tokens, const void* ta
   MEDUSA_REQUIRE(M >= 0 && d > 0 && V > 0, MEDUSA_ERR_ARG, "embed_rmsnorm: bad sizes");
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(tokens && table && w && x && y, MEDUSA_ERR_ARG, "embed_rmsnorm: null pointer");
+  // 16-byte pieces need aligned rows: d % 8 == 0 and 16-byte aligned bases
+  const bool vec = dtype == MEDUSA_BF16 && d % 8 == 0 && d <= 8192 &&
+                   (((uintptr_t)table | (uintptr_t)w | (uintptr_t)x | (uintptr_t)y) & 15) == 0;
   if (dtype == MEDUSA_F32)
-    hipLaunchKernelGGL(embed_rmsnorm_kernel<float>, dim3(M), dim3(256), 0, stream, d, tokens, (const float*)table, V,
-                       (const float*)w, eps, (float*)x, (float*)y);
+    hipLaunchKernelGGL((embed_rmsnorm_kernel<float, 0>), dim3(M), dim3(256), 0, stream, d, tokens,
+                       (const float*)table, V, (const float*)w, eps, (float*)x, (float*)y);
+  else if (!vec)
+    hipLaunchKernelGGL((embed_rmsnorm_kernel<bf16_t, 0>), dim3(M), dim3(256), 0, stream, d, tokens,
+                       (const bf16_t*)table, V, (const bf16_t*)w, eps, (bf16_t*)x, (bf16_t*)y);
+  else if (d <= 2048)
+    hipLaunchKernelGGL((embed_rmsnorm_kernel<bf16_t, 1>), dim3(M), dim3(256), 0, stream, d, tokens,
+                       (const bf16_t*)table, V, (const bf16_t*)w, eps, (bf16_t*)x, (bf16_t*)y);
+  else if (d <= 4096)
+    hipLaunchKernelGGL((embed_rmsnorm_kernel<bf16_t, 2>), dim3(M), dim3(256), 0, stream, d, tokens,
+                       (const bf16_t*)table, V, (const bf16_t*)w, eps, (bf16_t*)x, (bf16_t*)y);
   else
-    hipLaunchKernelGGL(embed_rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, stream, d, tokens, (const bf16_t*)table,
-                       V, (const bf16_t*)w, eps, (bf16_t*)x, (bf16_t*)y);
+    hipLaunchKernelGGL((embed_rmsnorm_kernel<bf16_t, 4>), dim3(M), dim3(256), 0, stream, d, tokens,
+                       (const bf16_t*)table, V, (const bf16_t*)w, eps, (bf16_t*)x, (bf16_t*)y);
   return check_launch("embed_rmsnorm");
 }
 
