@@ -287,16 +287,20 @@ __global__ __launch_bounds__(NW * 64) void attn_lds_kernel(
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sr[e]);
     return halves_max(mx) * scale_log2;
   };
+  // Rescales are rare once the running maxima settle, but each lane holds its own
+  // row, so a per-lane branch would be if-converted into 64 multiplies (and an
+  // exponential) on every unit.  A wave-wide vote skips the whole block unless
+  // some lane needs it; lanes that do not keep a factor of 1.
   auto rescale = [&](float mt) __attribute__((always_inline)) {
-    if (mt > mrun + RESCALE_SLACK) {
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mt);
-      lrun *= alpha;
+    const bool need = mt > mrun + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(need) == 0) return;
+    const float alpha = need ? __builtin_amdgcn_exp2f(mrun - mt) : 1.0f;
+    lrun *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      mrun = mt;
-    }
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    mrun = need ? mt : mrun;
   };
   // P^T B operand: k-slot t of lane half hh <-> key 16*ksub + 8*(t/4) + 4*hh + t%4,
   // the same key order as the transposed V^T fragment.  The row sum is a
