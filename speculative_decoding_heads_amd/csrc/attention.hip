@@ -20,6 +20,7 @@
 //  * attn_stream (attn_stream.hip) -- bf16, head size 64 or 128, the
 //    streaming MFMA kernel; with KV splits it writes fp32 partials that
 //    attn_combine (below) merges.
+#include <math.h>
 #include <stdlib.h>
 
 #include <mutex>
@@ -196,27 +197,45 @@ struct MfmaPlan {
 
 MfmaPlan mfma_plan_nw(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint, int nw);
 
-// Waves per workgroup: the largest of 8, 4, 2 whose plan puts >= 256
-// workgroups on the chip (one per CU), else the one with the most workgroups
-// (larger on a tie).  Fewer waves mean 32-row chunks of fewer query rows and so
-// more workgroups when batch x KV heads is small (batch 1 with shared KV heads:
-// 8 x 8 splits at 8 waves, 256 workgroups at 2); where 8 waves already fill the
-// chip they measure faster.  MEDUSA_ATTN_WAVES = 2 | 4 | 8 forces a count.
+// Waves per workgroup and KV splits.  For each width nw in {8, 4, 2} the split
+// count is the one that puts a workgroup on each of the 256 CUs, kept to at
+// least 4 64-key tiles per split (mfma_plan_nw).  Among the widths whose plan
+// fills the chip, the one whose splits run closest to 16 tiles (log scale;
+// ties: more waves); if none fills, the one with the most workgroups (ties:
+// more waves).  The two costs it trades: every split writes fp32 partials of
+// all R query rows of its KV head (R x Dh x 4 bytes, at 4 tiles a split about
+// what the split reads of K/V) that the merge reads back, and fewer waves mean
+// more 32-row chunks, each streaming the same K/V again.  Measured on MI355X
+// over batch 1 and 8, 8 and 32 KV heads x 128, prefixes 1k-64k and every
+// (waves, splits) pair: within 1 % of the best pair summed over the cases, the
+// worst case 15 % off (batch 1, 8 KV heads, prefix 8k).  MEDUSA_ATTN_WAVES =
+// 2 | 4 | 8 forces a width.
 MfmaPlan mfma_plan(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint) {
   const int forced = attn_stream_waves_forced();
   if (forced) return mfma_plan_nw(B, T, Hq, Hkv, Dh, L_hint, forced);
-  MfmaPlan best{};
-  int64_t best_wgs = -1;
+  const int64_t tiles = (L_hint + ATTN_KT - 1) / ATTN_KT;
+  MfmaPlan fill{}, most{};
+  double fill_d = 0.0;
+  int64_t most_wgs = -1;
+  bool any_fill = false;
   for (int nw : {8, 4, 2}) {
     const MfmaPlan p = mfma_plan_nw(B, T, Hq, Hkv, Dh, L_hint, nw);
     const int64_t wgs = (int64_t)p.n_splits * Hkv * B * p.n_rchunks;
-    if (wgs >= 256) return p;
-    if (wgs > best_wgs) {
-      best = p;
-      best_wgs = wgs;
+    if (wgs >= 256) {
+      const int64_t tps = (tiles + p.n_splits - 1) / p.n_splits;
+      const double d = fabs(log2((double)(tps > 0 ? tps : 1) / 16.0));
+      if (!any_fill || d < fill_d) {
+        fill = p;
+        fill_d = d;
+        any_fill = true;
+      }
+    }
+    if (wgs > most_wgs) {
+      most = p;
+      most_wgs = wgs;
     }
   }
-  return best;
+  return any_fill ? fill : most;
 }
 
 MfmaPlan mfma_plan_nw(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint, int nw) {
@@ -227,15 +246,15 @@ MfmaPlan mfma_plan_nw(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint, int
   p.n_rchunks = (R + rows_wg - 1) / rows_wg;
   const int64_t tiles = (L_hint + ATTN_KT - 1) / ATTN_KT;
   const int64_t units = (int64_t)B * Hkv * p.n_rchunks;
-  // aim at ~8 waves per CU (256 CUs), each split at least 2 tiles
-  // (MEDUSA_ATTN_MIN_TILES overrides the 2 for tuning runs)
+  // one workgroup per CU (256), each split at least min_tiles tiles
+  // (MEDUSA_ATTN_MIN_TILES overrides the 4 for tuning runs)
   static const int min_tiles = [] {
     const char* e = getenv("MEDUSA_ATTN_MIN_TILES");
-    const int v = e ? atoi(e) : 2;
-    return v >= 1 ? v : 2;
+    const int v = e ? atoi(e) : 4;
+    return v >= 1 ? v : 4;
   }();
-  int64_t s = (2048 / nw + units - 1) / units;
-  int64_t smax = (tiles + min_tiles - 1) / min_tiles;
+  int64_t s = (256 + units - 1) / units;
+  int64_t smax = tiles / min_tiles;
   if (smax > ATTN_MAX_SPLITS) smax = ATTN_MAX_SPLITS;
   if (s > smax) s = smax;
   if (s < 1) s = 1;

@@ -49,6 +49,8 @@ def _run(dev, choices, B, Hq, Hkv, Dh, L, Lmax, dtype_name, seed, ragged=False, 
     (chain_choices(11), 1, 32, 2, 2000, 2048, False),    # G = 16: 192 rows, a chain tree
     (seeded_tree_choices(0), 1, 32, 32, 1024, 1088, False),  # MHA 64 rows (7B shape)
     (seeded_tree_choices(0), 2, 32, 8, 1024, 1024, True),  # split KV over ragged 1k prefixes
+    (seeded_tree_choices(0), 1, 32, 8, 16384, 16384, False),  # 4 waves, two row chunks, 16 splits
+    (seeded_tree_choices(0), 8, 32, 8, 2048, 2048, True),  # batch 8: 4 waves, 2 splits
 ])
 def test_bf16_mfma_parity(dev, choices, B, Hq, Hkv, L, Lmax, ragged):
     got, ref = _run(dev, choices, B, Hq, Hkv, 128, L, Lmax, "bf16", seed=L + B, ragged=ragged)
