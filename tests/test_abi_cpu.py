@@ -1,5 +1,6 @@
 """CPU checks of the C ABI: the library loads, exports every function the headers
-declare, and the host tree builder equals the oracle's tree buffers (no GPU needed)."""
+declare, the host tree builder equals the oracle's tree buffers, and the attention
+launch plan picks the measured split counts (no GPU needed)."""
 import ctypes as C
 import glob
 import os
@@ -88,3 +89,29 @@ def test_status_message_is_set():
     L, lib = _lib()
     _host_tree([(0,), (0,)])
     assert b"duplicate" in lib.medusa_last_error()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,splits", [
+    (1, 32, 8, 1024, 4),    # 2 waves x 4 row chunks, 4 splits: 128 workgroups, none fills the chip
+    (1, 32, 8, 2048, 8),    # 2 waves, 8 splits of 4 tiles: 256 workgroups
+    (1, 32, 8, 16384, 16),  # 4 waves (2 row chunks), 16 splits of 16 tiles
+    (1, 32, 8, 65536, 32),  # 8 waves, 32 splits of 32 tiles
+    (8, 32, 8, 1024, 1),    # batch 8: 2 waves x 4 row chunks fill the chip unsplit
+    (8, 32, 8, 2048, 2),    # 4 waves, 2 splits of 16 tiles
+    (8, 32, 8, 65536, 4),   # 8 waves, 4 splits
+    (1, 32, 32, 1152, 4),   # 32 KV heads, 18 tiles: at least 4 tiles a split
+    (1, 32, 32, 65536, 8),  # 32 KV heads, 8 splits fill the chip
+])
+def test_attention_launch_plan_splits(B, Hq, Hkv, L, splits):
+    """The KV split count of the bf16 attention launch plan (a 64-node tree, head size
+    128), read back from the workspace size: fp32 partials of every query row of every
+    split plus their maxima and sums, none when unsplit."""
+    _, lib = _lib()
+    T, Dh = 64, 128
+    R = T * (Hq // Hkv)
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    expect = 0 if splits == 1 else up(B * Hkv * splits * R * Dh * 4) + up(B * Hkv * splits * R * 2 * 4)
+    assert lib.tree_attention_workspace_size(1, B, T, Hq, Hkv, Dh, L) == expect
