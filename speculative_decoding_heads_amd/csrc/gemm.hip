@@ -250,14 +250,40 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[NR][MB], int n0, i
     }
 }
 
+// Positions of a lane's four rows (m0 + 16j + l16; rows past M read row M-1's)
+// for the rotary epilogue, which clamps them.  The kernels load them before the
+// product loop and use them only in the epilogue, so the loads complete under
+// the loop and the table loads need no dependent round trip.
+__device__ __forceinline__ void rope_positions(const EpiArgs& e, int m0, int M, int l16, int (&p)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = e.pos[min(m0 + j * 16 + l16, M - 1)];
+}
+
 // Rotary embedding + q / K / V split for a wave's 16 x 64 tile of the fused
 // projection (tile mapping of EPI_QKV_ROPE in gemm_lds_kernel).  The partner
 // tile (wave w ^ 1) is exchanged through LDS; every wave of the workgroup
 // calls this (it holds two barriers).  Rotate-half: for i < Dh/2,
 // y[i] = x[i] cos - x[i + Dh/2] sin, y[i + Dh/2] = x[i + Dh/2] cos + x[i] sin,
-// at the row's position (clamped to [0, max_pos)); V rows are stored as they are.
+// at the row's position p (rope_positions), clamped to [0, max_pos); V rows
+// are stored as they are.
+// The cos / sin loads go out before the exchange and land during it.
 __device__ __forceinline__ void rope_epilogue(const f32x4 (&acc)[1][4], char* lds, int w, int n0, int m0, int M,
-                                              const EpiArgs& e, int l16, int lg) {
+                                              const EpiArgs& e, int l16, int lg, const int (&p)[4]) {
+  const int Dh = e.Dh, half = Dh / 2;
+  const int hd = n0 / Dh, within = n0 % Dh;
+  const int hf = within >= half;                     // second half of the head
+  const int i0 = (hf ? within - half : within) + 4 * lg;  // first of this lane's 4 dims (in the half)
+  const bool rot = hd < e.Hq + e.Hkv;                // q or K rows (wave-uniform)
+  float cs[4][4], sn[4][4];
+  if (rot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pj = p[j] < 0 ? 0 : (p[j] >= e.max_pos ? e.max_pos - 1 : p[j]);
+      const size_t off = (size_t)pj * half + i0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs[j][r] = e.cos_t[off + r], sn[j][r] = e.sin_t[off + r];
+    }
+  }
   float* xs = (float*)lds;  // [4 waves][16 rows][64 columns]
   __syncthreads();          // every wave is done with the A buffers
 #pragma unroll
@@ -265,10 +291,6 @@ __device__ __forceinline__ void rope_epilogue(const f32x4 (&acc)[1][4], char* ld
 #pragma unroll
     for (int r = 0; r < 4; ++r) xs[(w * 16 + 4 * lg + r) * 64 + j * 16 + l16] = acc[0][j][r];
   __syncthreads();
-  const int Dh = e.Dh, half = Dh / 2;
-  const int hd = n0 / Dh, within = n0 % Dh;
-  const int hf = within >= half;                     // second half of the head
-  const int i0 = (hf ? within - half : within) + 4 * lg;  // first of this lane's 4 dims (in the half)
   const int partner = w ^ 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -277,16 +299,13 @@ __device__ __forceinline__ void rope_epilogue(const f32x4 (&acc)[1][4], char* ld
     const int b = m / e.T, t = m % e.T;
     float y[4];
     bf16_t* dst;
-    if (hd < e.Hq + e.Hkv) {
-      int p = e.pos[m];
-      p = p < 0 ? 0 : (p >= e.max_pos ? e.max_pos - 1 : p);
+    if (rot) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float own = acc[0][j][r];
         const float par = xs[(partner * 16 + 4 * lg + r) * 64 + j * 16 + l16];
-        const float c = e.cos_t[(size_t)p * half + i0 + r], sn = e.sin_t[(size_t)p * half + i0 + r];
         // first half: own = x[i], par = x[i + half]; second half: the reverse
-        y[r] = hf ? own * c + par * sn : own * c - par * sn;
+        y[r] = hf ? own * cs[j][r] + par * sn[j][r] : own * cs[j][r] - par * sn[j][r];
       }
       const int dim = hf * half + i0;
       dst = hd < e.Hq ? e.q_out + (((size_t)b * e.T + t) * e.Hq + hd) * Dh + dim
@@ -483,6 +502,9 @@ __global__ __launch_bounds__(NWV * 64) void gemm_lds_kernel(int M, int N, int K,
     }
   }
   const int m0 = mt * GM;
+  // rotary rows' positions, loaded ahead of the product loop
+  int rpos[4] = {0, 0, 0, 0};
+  if (rope) rope_positions(e, m0, M, l16, rpos);
   const int nchunks = (K / GK) / U;
   const int c0 = (int)((int64_t)nchunks * ks / SK), c1 = (int)((int64_t)nchunks * (ks + 1) / SK);
   const int per = c1 - c0;  // chunks of this workgroup (uniform)
@@ -604,7 +626,7 @@ __global__ __launch_bounds__(NWV * 64) void gemm_lds_kernel(int M, int N, int K,
   }
   if constexpr (NR == 1 && (NWV == 4 || NWV == 3)) {
     if (rope) {
-      rope_epilogue(acc, lds, w, n0, m0, M, e, l16, lg);
+      rope_epilogue(acc, lds, w, n0, m0, M, e, l16, lg, rpos);
       return;
     }
   }
@@ -678,6 +700,9 @@ __global__ __launch_bounds__(NWV * 64) void gemm_dma_kernel(int M, int N, int K,
     }
   }
   const int m0 = mt * GM;
+  // rotary rows' positions, loaded ahead of the product loop
+  int rpos[4] = {0, 0, 0, 0};
+  if (rope) rope_positions(e, m0, M, l16, rpos);
   const int nchunks = K / KC;
   const int c0 = (int)((int64_t)nchunks * ks / SK), c1 = (int)((int64_t)nchunks * (ks + 1) / SK);
   const int per = c1 - c0;
@@ -763,7 +788,7 @@ __global__ __launch_bounds__(NWV * 64) void gemm_dma_kernel(int M, int N, int K,
   }
   if constexpr (NR == 1 && (NWV == 4 || NWV == 3)) {
     if (rope) {
-      rope_epilogue(acc, sm, w, n0, m0, M, e, l16, lg);
+      rope_epilogue(acc, sm, w, n0, m0, M, e, l16, lg, rpos);
       return;
     }
   }

@@ -412,7 +412,9 @@ def test_bf16_fused_step_carry_and_state(dev):
             rl = ref[b, k]
             ri = topk_desc(rl, K)
             assert len(set(gi[b, k].tolist())) == K
-            tol = 1e-2 * np.abs(rl).max()
+            # the carried ranks hold the true ranks' logits to the bf16 bound
+            # (1e-2 absolute + 2e-2 relative): only near-ties may swap
+            tol = 1e-2 + 2e-2 * np.abs(rl[ri])
             assert np.all(np.abs(rl[gi[b, k]] - rl[ri]) <= tol), (b, k)
 
 
