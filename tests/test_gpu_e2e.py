@@ -219,11 +219,12 @@ BF16_TOL = dict(rtol=2e-2, atol=1e-2)
 E2E_LOGIT_ATOL = 5e-2
 
 
-def _forward_parity(dev, model, params, tok, pos, gKc, gVc, seq, tree, ot, Lmax, Kc, Vc):
+def _forward_parity(dev, model, params, tok, pos, gKc, gVc, seq, tree, ot, Lmax, Kc, Vc, oracle_pos=None):
     """bf16 forward against the oracle: every stage of every layer on the GPU's own
     input to it (conditional, stated tolerance), the final norm and LM head on the
     GPU's last stream, and the whole stack from the tokens (unconditional, measured
-    bound)."""
+    bound).  oracle_pos: the positions the oracle runs at (default: those given to
+    the GPU)."""
     import torch
     from oracle.decoder import embed_tokens, final_logits
     NL, B, T = len(params["layers"]), tok.shape[0], tok.shape[1]
@@ -231,7 +232,8 @@ def _forward_parity(dev, model, params, tok, pos, gKc, gVc, seq, tree, ot, Lmax,
     logits, h, Kt, Vt = model.forward(tok, pos, gKc, gVc, seq, tree, L_hint=Lmax, trace=trace)
     torch.cuda.synchronize()
     tr = {k: to_np(v).astype(np.float64) for k, v in trace.items()}
-    toks, pos_np, seq_np = to_np(tok), to_np(pos), to_np(seq)
+    toks, seq_np = to_np(tok), to_np(seq)
+    pos_np = to_np(pos) if oracle_pos is None else oracle_pos
     assert_close(tr["x"][0].reshape(B, T, -1), embed_tokens(params, toks, bf16=True), rtol=0, atol=0,
                  what="embedding rows")
     gK, gV = to_np(Kt), to_np(Vt)
@@ -294,6 +296,38 @@ def test_bf16_forward_vs_oracle(dev, heads_kv_dim, B, tree_name):
     d = lambda x: torch.from_numpy(x).to(dev)
     _forward_parity(dev, model, params, d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev),
                     to_dev(Vc, torch.bfloat16, dev), d(seq), tree, ot, Lmax, Kc, Vc)
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_bf16_forward_clamps_rotary_positions(dev, B):
+    """Positions outside the rotary table's [0, max_pos) are clamped (medusa_model.h):
+    the fused projection's rotary epilogue (48-row workgroups at batch 1, 64-row at
+    batch 2) equals the oracle run at the clamped positions."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd.model import Model
+    say("e2e bf16 forward, rotary positions clamped, batch", B)
+    (params, heads), Cfg = _small_bf16_model(5, (4, 4, 128))
+    P, H = _upload(params, heads, torch.bfloat16, dev)
+    max_pos = 152
+    model = Model(P, H, max_pos=max_pos)
+    tree = api.Tree(PAGE_TREE_CHOICES)
+    ot = tree_buffers(PAGE_TREE_CHOICES)
+    rng = np.random.default_rng(6)
+    L, Lmax = 150, 192
+    NL, Hkv, Dh = Cfg.n_layers, Cfg.n_kv_heads, Cfg.head_dim
+    from workloads import bf16_round
+    Kc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
+    Vc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
+    seq = np.array([L, L - 37][:B], np.int32)
+    toks = rng.integers(0, Cfg.vocab, (B, ot["T"])).astype(np.int32)
+    pos = (seq[:, None] + ot["depth"][None, :]).astype(np.int32)  # batch 0 reaches 154
+    pos[0, ::9] = -3 - np.arange(pos[0, ::9].size)                  # and some negative
+    assert (pos >= max_pos).any() and (pos < 0).any()
+    d = lambda x: torch.from_numpy(x).to(dev)
+    _forward_parity(dev, model, params, d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev),
+                    to_dev(Vc, torch.bfloat16, dev), d(seq), tree, ot, Lmax, Kc, Vc,
+                    oracle_pos=np.clip(pos, 0, max_pos - 1))
 
 
 def test_bf16_forward_full_width_layer(dev):
