@@ -68,6 +68,32 @@ def test_bf16_many_splits(dev):
     assert_close(got, ref, what="bf16 splits", **BF16_TOL)
 
 
+@pytest.mark.parametrize("lens", [(8192, 300), (0, 5000)])
+def test_bf16_splits_without_prefix_tiles(dev, lens):
+    """The split plan follows L_hint (8192); a sequence much shorter than it leaves
+    splits with no prefix tile at all (only the last split holds the tree tile), whose
+    empty partials the merge must weigh zero.  Cache rows past each length are NaN."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("tree_attention empty splits", lens)
+    B, Hq, Hkv, Dh, Lmax = 2, 32, 8, 128, 8192
+    tree = api.Tree(seeded_tree_choices(0))
+    q, Kc, Vc, Kt, Vt, _ = attention_inputs(31, B, tree.T, Hq, Hkv, Dh, Lmax, Lmax)
+    seq = np.array(lens, np.int32)
+    for b in range(B):
+        Kc[b, :, seq[b]:] = np.nan
+        Vc[b, :, seq[b]:] = np.nan
+    assert api.tree_attention_workspace_size(1, B, tree.T, Hq, Hkv, Dh, Lmax) > 0  # a split plan
+    scale = 1.0 / np.sqrt(Dh)
+    out = api.tree_attention(to_dev(q, torch.bfloat16, dev), to_dev(Kc, torch.bfloat16, dev),
+                             to_dev(Vc, torch.bfloat16, dev), torch.from_numpy(seq).to(dev),
+                             to_dev(Kt, torch.bfloat16, dev), to_dev(Vt, torch.bfloat16, dev), tree, scale,
+                             L_hint=Lmax)
+    torch.cuda.synchronize()
+    ref = oracle_attn(q, Kc, Vc, seq, Kt, Vt, tree_buffers(seeded_tree_choices(0))["anc"], scale)
+    assert_close(to_np(out), ref, what="bf16 empty splits", **BF16_TOL)
+
+
 def test_bf16_generic_head_size(dev):
     got, ref = _run(dev, TWO_HEAD_CHOICES, 2, 8, 2, 32, 90, 100, "bf16", seed=3, ragged=True)
     assert_close(got, ref, what="bf16 generic", **BF16_TOL)
