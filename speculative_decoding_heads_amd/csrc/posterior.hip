@@ -35,9 +35,16 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
   }
 }
 
+// NV > 0 (vec rows of at most NV * 4 * kStatThreads entries): the row is held in
+// registers, NV float4 a thread, every load issued before the first use, and pass
+// 2 reads no memory; NV == 0 streams the row twice (the second time from L2).
+// Each thread visits its entries in the same order either way (thread tid owns
+// float4 tid, tid + kStatThreads, ...), so the results are the same.  vec: the
+// rows are 16-byte aligned (V % 4 == 0 and an aligned base).
+template <int NV>
 __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* __restrict__ logits, int T, int V,
-                                                                 int typical, float inv_tau, float eps, float delta,
-                                                                 NodeStat* __restrict__ out) {
+                                                                 int vec, int typical, float inv_tau, float eps,
+                                                                 float delta, NodeStat* __restrict__ out) {
   const int u = blockIdx.x, b = blockIdx.y;
   const float* x = logits + ((size_t)b * T + u) * V;
   const int tid = threadIdx.x;
@@ -45,6 +52,16 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
   __shared__ int s_i[kStatThreads / 64];
   __shared__ float s_f[kStatThreads / 64];
   const int lane = tid & 63, w = tid >> 6;
+  const int V4 = V / 4;
+  float4 f[NV > 0 ? NV : 1];
+  if constexpr (NV > 0) {
+    const float4* x4 = (const float4*)x;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int k4 = tid + j * kStatThreads;
+      f[j] = x4[k4 < V4 ? k4 : V4 - 1];  // a clamped index, not a branch: the loads go out together
+    }
+  }
 
   // pass 1: argmax, and for typical an online sum of exp((x - running max)/tau),
   // as 2^((x - max) * log2(e)/tau) on the hardware base-2 exponential
@@ -61,15 +78,25 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
       z += __builtin_amdgcn_exp2f((v - bv) * c2);
     }
   };
-  const bool vec = (V % 4) == 0;
-  if (vec) {
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int k4 = tid + j * kStatThreads;
+      if (k4 < V4) {
+        visit(f[j].x, 4 * k4);
+        visit(f[j].y, 4 * k4 + 1);
+        visit(f[j].z, 4 * k4 + 2);
+        visit(f[j].w, 4 * k4 + 3);
+      }
+    }
+  } else if (vec) {
     const float4* x4 = (const float4*)x;
-    for (int k4 = tid; k4 < V / 4; k4 += kStatThreads) {
-      const float4 f = x4[k4];
-      visit(f.x, 4 * k4);
-      visit(f.y, 4 * k4 + 1);
-      visit(f.z, 4 * k4 + 2);
-      visit(f.w, 4 * k4 + 3);
+    for (int k4 = tid; k4 < V4; k4 += kStatThreads) {
+      const float4 g = x4[k4];
+      visit(g.x, 4 * k4);
+      visit(g.y, 4 * k4 + 1);
+      visit(g.z, 4 * k4 + 2);
+      visit(g.w, 4 * k4 + 3);
     }
   } else {
     for (int k = tid; k < V; k += kStatThreads) visit(x[k], k);
@@ -109,14 +136,25 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
     const float q = __builtin_amdgcn_exp2f((v - m) * c2) * invZ;
     hsum += q * __builtin_amdgcn_logf(q + 1e-5f);
   };
-  if (vec) {
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int k4 = tid + j * kStatThreads;
+      if (k4 < V4) {
+        hterm(f[j].x);
+        hterm(f[j].y);
+        hterm(f[j].z);
+        hterm(f[j].w);
+      }
+    }
+  } else if (vec) {
     const float4* x4 = (const float4*)x;
-    for (int k4 = tid; k4 < V / 4; k4 += kStatThreads) {
-      const float4 f = x4[k4];
-      hterm(f.x);
-      hterm(f.y);
-      hterm(f.z);
-      hterm(f.w);
+    for (int k4 = tid; k4 < V4; k4 += kStatThreads) {
+      const float4 g = x4[k4];
+      hterm(g.x);
+      hterm(g.y);
+      hterm(g.z);
+      hterm(g.w);
     }
   } else {
     for (int k = tid; k < V; k += kStatThreads) hterm(x[k]);
@@ -221,8 +259,17 @@ extern "C" int evaluate_posterior(const medusa_tree* t, int B, int V, const floa
   NodeStat* st = (NodeStat*)ws;
   const int typical = mode == MEDUSA_TYPICAL;
   const float inv_tau = typical ? 1.0f / temperature : 1.0f;
-  hipLaunchKernelGGL(node_stats_kernel, dim3(T, B), dim3(kStatThreads), 0, stream, logits, T, V, typical, inv_tau,
-                     eps, delta, st);
+  const int vec = V % 4 == 0 && ((uintptr_t)logits & 15) == 0;
+  const int nv = vec ? (V / 4 + kStatThreads - 1) / kStatThreads : 0;
+#define NS_LAUNCH(NVV)                                                                                        \
+  hipLaunchKernelGGL(node_stats_kernel<NVV>, dim3(T, B), dim3(kStatThreads), 0, stream, logits, T, V, vec,  \
+                     typical, inv_tau, eps, delta, st)
+  if (nv == 1) NS_LAUNCH(1);
+  else if (nv == 2) NS_LAUNCH(2);
+  else if (nv == 3 || nv == 4) NS_LAUNCH(4);
+  else if (nv >= 5 && nv <= 8) NS_LAUNCH(8);
+  else NS_LAUNCH(0);  // unaligned rows, or rows past 8 * 4 * kStatThreads entries
+#undef NS_LAUNCH
   int rc = check_launch("evaluate_posterior stats");
   if (rc) return rc;
   hipLaunchKernelGGL(select_kernel, dim3(B), dim3(64), 0, stream, t->dev, logits, V, tree_tokens, typical, inv_tau,

@@ -25,7 +25,8 @@
 // bisects the probability threshold over the float bit patterns (31 passes of
 // the mass at or above a candidate threshold, from L2); a last pass generates
 // the uniforms and keeps the best allowed score.  Rows are read with float4
-// loads when V % 4 == 0.
+// loads when V % 4 == 0 and the rows are 16-byte aligned, and held in registers
+// when V <= 32768.
 #include "common.h"
 #include "medusa_model.h"
 #include "tree_dev.h"
@@ -74,6 +75,7 @@ struct DrawArgs {
   const float* logits;
   int64_t ld;
   int V;
+  int vec;             // rows read as float4: V % 4 == 0, ld % 4 == 0, 16-byte aligned base
   const int32_t* seq;  // nullable: the sequence of row r is r / rows_per_seq
   int rows_per_seq;
   const int32_t* pos;
@@ -83,15 +85,44 @@ struct DrawArgs {
   int32_t* out;
 };
 
+// NV > 0 (float4 rows of at most NV * 4 * kDrawThreads entries): the row and its
+// probabilities q are held in registers, NV float4 a thread, loaded once; the
+// entropy pass, the nucleus bisection and the draw then read no memory.  NV == 0
+// reads the row from memory in every pass (from L2 after the first).  Each
+// thread visits its entries in the same order either way (thread tid owns float4
+// tid, tid + kDrawThreads, ...) and q is the same function of the logit, so the
+// draws are the same.
+template <int NV>
 __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
   const int row = blockIdx.x;
   const float* x = a.logits + (size_t)row * a.ld;
   const int V = a.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool vec = (V % 4) == 0 && (a.ld % 4) == 0;
+  const bool vec = NV > 0 || a.vec;
+  const int V4 = V / 4;
   __shared__ float s_v[kDrawWaves], s_f[kDrawWaves];
   __shared__ int s_i[kDrawWaves];
   __shared__ float red[kDrawWaves];
   const float c2 = a.inv_tau * 1.4426950408889634f;
+  float4 f[NV > 0 ? NV : 1];
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int k4 = tid + i * kDrawThreads;
+      f[i] = ((const float4*)x)[k4 < V4 ? k4 : V4 - 1];  // a clamped index: the loads go out together
+    }
+  }
+  // fn(v, k4) on each float4 of this thread's stripe, in stripe order (vec rows)
+  auto each4 = [&](auto&& fn) __attribute__((always_inline)) {
+    if constexpr (NV > 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int k4 = tid + i * kDrawThreads;
+        if (k4 < V4) fn(f[i], k4, i);
+      }
+    } else {
+      for (int k4 = tid; k4 < V4; k4 += kDrawThreads) fn(((const float4*)x)[k4], k4, 0);
+    }
+  };
 
   // ---- pass 1: argmax (lowest index on ties), max, Z
   float bv = -INFINITY, z = 0.f;
@@ -106,13 +137,12 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
     }
   };
   if (vec) {
-    for (int k4 = tid; k4 < V / 4; k4 += kDrawThreads) {
-      const float4 f = ((const float4*)x)[k4];
-      visit(f.x, 4 * k4);
-      visit(f.y, 4 * k4 + 1);
-      visit(f.z, 4 * k4 + 2);
-      visit(f.w, 4 * k4 + 3);
-    }
+    each4([&](float4 g, int k4, int) {
+      visit(g.x, 4 * k4);
+      visit(g.y, 4 * k4 + 1);
+      visit(g.z, 4 * k4 + 2);
+      visit(g.w, 4 * k4 + 3);
+    });
   } else {
     for (int k = tid; k < V; k += kDrawThreads) visit(x[k], k);
   }
@@ -141,6 +171,16 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
   if (bi == 0x7fffffff) bi = 0;
   const float m = bv, invZ = 1.0f / z;
   auto qof = [&](float v) { return __builtin_amdgcn_exp2f((v - m) * c2) * invZ; };
+  // q of the held entries (NV > 0), computed once
+  float4 qh[NV > 0 ? NV : 1];
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) qh[i] = make_float4(qof(f[i].x), qof(f[i].y), qof(f[i].z), qof(f[i].w));
+  }
+  auto q4 = [&](float4 g, int i) __attribute__((always_inline)) {
+    if constexpr (NV > 0) return qh[i];
+    else return make_float4(qof(g.x), qof(g.y), qof(g.z), qof(g.w));
+  };
 
   // ---- the allow set: q > eta (typical) or q >= t (nucleus)
   float thr = 0.f;
@@ -148,12 +188,11 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
   if (a.kind == MEDUSA_SAMPLE_TYPICAL) {
     float hs = 0.f;
     if (vec) {
-      for (int k4 = tid; k4 < V / 4; k4 += kDrawThreads) {
-        const float4 f = ((const float4*)x)[k4];
-        const float q0 = qof(f.x), q1 = qof(f.y), q2 = qof(f.z), q3 = qof(f.w);
-        hs += q0 * __builtin_amdgcn_logf(q0 + 1e-5f) + q1 * __builtin_amdgcn_logf(q1 + 1e-5f) +
-              q2 * __builtin_amdgcn_logf(q2 + 1e-5f) + q3 * __builtin_amdgcn_logf(q3 + 1e-5f);
-      }
+      each4([&](float4 g, int, int i) {
+        const float4 q = q4(g, i);
+        hs += q.x * __builtin_amdgcn_logf(q.x + 1e-5f) + q.y * __builtin_amdgcn_logf(q.y + 1e-5f) +
+              q.z * __builtin_amdgcn_logf(q.z + 1e-5f) + q.w * __builtin_amdgcn_logf(q.w + 1e-5f);
+      });
     } else {
       for (int k = tid; k < V; k += kDrawThreads) {
         const float q = qof(x[k]);
@@ -173,11 +212,10 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
       const float t = __uint_as_float(mid);
       float s = 0.f;
       if (vec) {
-        for (int k4 = tid; k4 < V / 4; k4 += kDrawThreads) {
-          const float4 f = ((const float4*)x)[k4];
-          const float q0 = qof(f.x), q1 = qof(f.y), q2 = qof(f.z), q3 = qof(f.w);
-          s += (q0 >= t ? q0 : 0.f) + (q1 >= t ? q1 : 0.f) + (q2 >= t ? q2 : 0.f) + (q3 >= t ? q3 : 0.f);
-        }
+        each4([&](float4 g, int, int i) {
+          const float4 q = q4(g, i);
+          s += (q.x >= t ? q.x : 0.f) + (q.y >= t ? q.y : 0.f) + (q.z >= t ? q.z : 0.f) + (q.w >= t ? q.w : 0.f);
+        });
       } else {
         for (int k = tid; k < V; k += kDrawThreads) {
           const float q = qof(x[k]);
@@ -198,8 +236,7 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
   const uint32_t p = (uint32_t)a.pos[row];
   float bs = -INFINITY;
   int bt = 0x7fffffff;
-  auto take = [&](float v, int k, uint32_t r) {
-    const float q = qof(v);
+  auto take = [&](float v, float q, int k, uint32_t r) {
     const bool ok = strict ? q > thr : q >= thr;
     if (!ok) return;
     const float s = (v - m) * a.inv_tau - logf(-logf(u01(r)));
@@ -208,20 +245,24 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
       bt = k;
     }
   };
-  for (int j = tid; j < (V + 3) / 4; j += kDrawThreads) {
-    const uint4 r = philox4x32_10(make_uint4((uint32_t)j, p, (uint32_t)seq, 0u), a.k0, a.k1);
-    const int k = 4 * j;
-    if (vec) {
-      const float4 f = ((const float4*)x)[j];
-      take(f.x, k, r.x);
-      take(f.y, k + 1, r.y);
-      take(f.z, k + 2, r.z);
-      take(f.w, k + 3, r.w);
-    } else {
-      if (k < V) take(x[k], k, r.x);
-      if (k + 1 < V) take(x[k + 1], k + 1, r.y);
-      if (k + 2 < V) take(x[k + 2], k + 2, r.z);
-      if (k + 3 < V) take(x[k + 3], k + 3, r.w);
+  if (vec) {
+    each4([&](float4 g, int j, int i) {
+      const uint4 r = philox4x32_10(make_uint4((uint32_t)j, p, (uint32_t)seq, 0u), a.k0, a.k1);
+      const float4 q = q4(g, i);
+      const int k = 4 * j;
+      take(g.x, q.x, k, r.x);
+      take(g.y, q.y, k + 1, r.y);
+      take(g.z, q.z, k + 2, r.z);
+      take(g.w, q.w, k + 3, r.w);
+    });
+  } else {
+    for (int j = tid; j < (V + 3) / 4; j += kDrawThreads) {
+      const uint4 r = philox4x32_10(make_uint4((uint32_t)j, p, (uint32_t)seq, 0u), a.k0, a.k1);
+      const int k = 4 * j;
+      if (k < V) take(x[k], qof(x[k]), k, r.x);
+      if (k + 1 < V) take(x[k + 1], qof(x[k + 1]), k + 1, r.y);
+      if (k + 2 < V) take(x[k + 2], qof(x[k + 2]), k + 2, r.z);
+      if (k + 3 < V) take(x[k + 3], qof(x[k + 3]), k + 3, r.w);
     }
   }
   butterfly([&](auto S) {
@@ -249,6 +290,16 @@ __global__ __launch_bounds__(kDrawThreads) void draw_kernel(DrawArgs a) {
       }
     a.out[row] = bt == 0x7fffffff ? bi : bt;  // nothing allowed: the argmax
   }
+}
+
+// grid rows x kDrawThreads: the register-held row when it fits
+void launch_draw(unsigned rows, hipStream_t stream, const DrawArgs& a) {
+  const int nv = a.vec ? (a.V / 4 + kDrawThreads - 1) / kDrawThreads : 0;
+  if (nv == 1) hipLaunchKernelGGL(draw_kernel<1>, dim3(rows), dim3(kDrawThreads), 0, stream, a);
+  else if (nv == 2) hipLaunchKernelGGL(draw_kernel<2>, dim3(rows), dim3(kDrawThreads), 0, stream, a);
+  else if (nv == 3 || nv == 4) hipLaunchKernelGGL(draw_kernel<4>, dim3(rows), dim3(kDrawThreads), 0, stream, a);
+  else if (nv >= 5 && nv <= 8) hipLaunchKernelGGL(draw_kernel<8>, dim3(rows), dim3(kDrawThreads), 0, stream, a);
+  else hipLaunchKernelGGL(draw_kernel<0>, dim3(rows), dim3(kDrawThreads), 0, stream, a);
 }
 
 // One wave per sequence, lane p = path p: leading candidates equal to the draw at
@@ -304,6 +355,7 @@ DrawArgs draw_args(const medusa_sampling* s, const float* logits, int64_t ld, in
   a.logits = logits;
   a.ld = ld;
   a.V = V;
+  a.vec = V % 4 == 0 && ld % 4 == 0 && ((uintptr_t)logits & 15) == 0;
   a.seq = seq;
   a.rows_per_seq = rows_per_seq;
   a.pos = pos;
@@ -327,8 +379,7 @@ extern "C" int medusa_sample_tokens(const medusa_sampling* s, int M, int V, cons
   MEDUSA_REQUIRE(M >= 0 && V > 0 && ldx >= V, MEDUSA_ERR_ARG, "sample_tokens: bad sizes");
   if (M == 0) return MEDUSA_OK;
   MEDUSA_REQUIRE(logits && pos && out, MEDUSA_ERR_ARG, "sample_tokens: null pointer");
-  hipLaunchKernelGGL(draw_kernel, dim3(M), dim3(kDrawThreads), 0, stream,
-                     draw_args(s, logits, ldx, V, seq_id, 1, pos, out));
+  launch_draw((unsigned)M, stream, draw_args(s, logits, ldx, V, seq_id, 1, pos, out));
   return check_launch("sample_tokens");
 }
 
@@ -355,8 +406,7 @@ extern "C" int evaluate_posterior_sampled(const medusa_tree* t, int B, int V, co
                  "evaluate_posterior_sampled: workspace %zu < %zu", ws_bytes,
                  evaluate_posterior_sampled_workspace_size(B, T));
   int32_t* draws = (int32_t*)ws;
-  hipLaunchKernelGGL(draw_kernel, dim3(B * T), dim3(kDrawThreads), 0, stream,
-                     draw_args(s, logits, V, V, nullptr, T, tree_pos, draws));
+  launch_draw((unsigned)(B * T), stream, draw_args(s, logits, V, V, nullptr, T, tree_pos, draws));
   rc = check_launch("evaluate_posterior_sampled draws");
   if (rc) return rc;
   hipLaunchKernelGGL(select_match_kernel, dim3(B), dim3(64), 0, stream, t->dev, tree_tokens, draws, best, accept_len,
