@@ -396,7 +396,15 @@ __global__ void commit_step_kernel(int T, int d, const TY* __restrict__ h, const
   if (!appended[b]) return;
   int s = sel[b];
   s = s < 0 ? 0 : (s >= T ? T - 1 : s);
-  for (int n = threadIdx.x; n < d; n += blockDim.x) h_sel[(size_t)b * d + n] = h[((size_t)b * T + s) * d + n];
+  const TY* src = h + ((size_t)b * T + s) * d;
+  TY* dst = h_sel + (size_t)b * d;
+  // 16-byte pieces when the rows allow (d * sizeof(TY) % 16 == 0, aligned bases)
+  constexpr int PE = 16 / sizeof(TY);
+  if (d % PE == 0 && ((((uintptr_t)h) | ((uintptr_t)h_sel)) & 15) == 0) {
+    for (int n = threadIdx.x; n < d / PE; n += blockDim.x) ((uint4*)dst)[n] = ((const uint4*)src)[n];
+  } else {
+    for (int n = threadIdx.x; n < d; n += blockDim.x) dst[n] = src[n];
+  }
   if (threadIdx.x == 0) root[b] = next_root[b];
 }
 
