@@ -30,43 +30,54 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// Best (value desc, index asc) pair of a wave, in every lane, without LDS:
-// DPP permutations inside each row of 16 lanes (swap neighbours, swap pairs,
-// mirror within 8, mirror within 16), then the gfx950 row swaps (rows r and
-// r ^ 1, then halves) -- each step pairs every lane with one not yet merged.
-// The order is total on non-NaN values, so any merge tree gives the same pair.
+// Best (value desc, index asc) pair of a wave, in every lane, without LDS.  The
+// pair travels as one 64-bit key whose unsigned order is the selection order
+// (the value's bits made monotone above, the index complemented below), so each
+// step is one 64-bit compare: DPP permutations inside each row of 16 lanes
+// (swap neighbours, swap pairs, mirror within 8, mirror within 16), then the
+// gfx950 row swaps (rows r and r ^ 1, then halves) -- each step pairs every lane
+// with one not yet merged, and the maximum does not depend on the merge tree.
+// -0 is keyed as +0 (the two tie, as under ==) and NaN below every number.
+__device__ __forceinline__ uint64_t vi_key(float v, int i) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  u = v == v ? u : 0u;
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)i;
+}
+__device__ __forceinline__ void vi_unkey(uint64_t k, float& v, int& i) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  v = __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+  i = (int)~(uint32_t)k;
+}
 template <int CTRL>
-__device__ __forceinline__ void best_dpp(float& bv, int& bi) {
-  const float v2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
-  const int i2 = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
-  if (better(v2, i2, bv, bi)) {
-    bv = v2;
-    bi = i2;
-  }
+__device__ __forceinline__ uint64_t key_dpp(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+  const uint64_t p = ((uint64_t)hi << 32) | lo;
+  return p > k ? p : k;
 }
 // r[0], r[1] of a row swap with both operands the same register are the lane's
-// own value and its partner's, in some order
-__device__ __forceinline__ void best_of_swap(float& bv, int& bi, const __attribute__((ext_vector_type(2))) unsigned rv,
-                                             const __attribute__((ext_vector_type(2))) unsigned ri) {
-  bv = __uint_as_float(rv[0]);
-  bi = (int)ri[0];
-  const float v2 = __uint_as_float(rv[1]);
-  const int i2 = (int)ri[1];
-  if (better(v2, i2, bv, bi)) {
-    bv = v2;
-    bi = i2;
-  }
+// own value and its partner's, in an order that is the same for both halves
+template <int ROWS>
+__device__ __forceinline__ uint64_t key_swap(uint64_t k) {
+  const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+  const auto rl = ROWS == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                             : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto rh = ROWS == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                             : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const uint64_t a = ((uint64_t)rh[0] << 32) | rl[0], b = ((uint64_t)rh[1] << 32) | rl[1];
+  return a > b ? a : b;
 }
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-  best_dpp<0xB1>(bv, bi);   // quad_perm [1,0,3,2]
-  best_dpp<0x4E>(bv, bi);   // quad_perm [2,3,0,1]
-  best_dpp<0x141>(bv, bi);  // row_half_mirror
-  best_dpp<0x140>(bv, bi);  // row_mirror
-  best_of_swap(bv, bi, __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false),
-               __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false));
-  best_of_swap(bv, bi, __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false),
-               __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false));
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = key_dpp<0xB1>(k);   // quad_perm [1,0,3,2]
+  k = key_dpp<0x4E>(k);   // quad_perm [2,3,0,1]
+  k = key_dpp<0x141>(k);  // row_half_mirror
+  k = key_dpp<0x140>(k);  // row_mirror
+  k = key_swap<16>(k);
+  return key_swap<32>(k);
 }
+// (a -0 value comes back as +0)
+__device__ __forceinline__ void wave_best(float& bv, int& bi) { vi_unkey(wave_max_key(vi_key(bv, bi)), bv, bi); }
 
 // Per-lane sorted list (best first) of up to TK_MAX candidates.
 struct LaneList {
@@ -199,13 +210,18 @@ __global__ __launch_bounds__(64) void topk_stage2_kernel(int ncand, const float*
 // One workgroup of 1024 threads per row (rows of at most 8 * 4096 entries):
 // the whole row sits in registers (NV float4 batches a thread) and the top K
 // come out of three steps with no second launch.
-//  1. t = the K-th largest of the 1024 thread maxima (each wave's K largest
-//     lane maxima into LDS, then every wave ranks the 16 * K of them).  The K
+//  1. t = the K-th largest of the 1024 thread maxima: they go to LDS and one
+//     wave takes K rounds of a wave maximum over them (16 a lane), while the
+//     other waves wait at the barrier (sixteen waves ranking the same values
+//     would share the four SIMDs and each run four times slower).  The K
 //     threads behind those maxima hold K distinct entries >= t, so the row's
 //     K-th largest entry is >= t.
 //  2. Every entry >= t is appended to an LDS list (typically a few dozen).
 //  3. One wave takes K rounds of a (value desc, index asc) maximum over the
-//     list, each round over the entries strictly after the previous winner.
+//     list: with at most 64 entries each lane holds one as a 64-bit key
+//     (vi_key) and the winner of a round drops out; with more, each round
+//     re-reads the list and keeps the entries strictly after the previous
+//     winner.
 // If more than TR_CAP entries reach t (a plateau of equal values), step 3 runs
 // over every thread's registers instead, with a block-wide maximum per round.
 // Either way the result is the exact top K in that order.
@@ -219,7 +235,8 @@ __global__ __launch_bounds__(TR_THREADS) void topk_row_kernel(int V, const float
                                                               int32_t* __restrict__ idx, float* __restrict__ val) {
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* r = x + (size_t)row * V;
-  __shared__ float s_wk[TR_WAVES * TK_MAX];
+  __shared__ float s_tm[TR_THREADS];
+  __shared__ float s_t;
   __shared__ float s_cv[TR_CAP];
   __shared__ int s_ci[TR_CAP];
   __shared__ float s_rv[2][TR_WAVES];
@@ -252,46 +269,38 @@ __global__ __launch_bounds__(TR_THREADS) void topk_row_kernel(int V, const float
   float tm = -INFINITY;
 #pragma unroll
   for (int e = 0; e < NV * 4; ++e) tm = fmaxf(tm, v[e]);
-  {
-    float cur = tm;
+  s_tm[tid] = tm;
+  __syncthreads();
+  if (w == 0) {
+    // lane holds the maxima of threads lane + 64 q; lb = the best of them left
+    uint64_t lk[TR_WAVES];
+#pragma unroll
+    for (int q = 0; q < TR_WAVES; ++q) lk[q] = vi_key(s_tm[lane + 64 * q], lane + 64 * q);
+    auto lane_best = [&]() __attribute__((always_inline)) {
+      uint64_t b = lk[0];
+#pragma unroll
+      for (int q = 1; q < TR_WAVES; ++q) b = lk[q] > b ? lk[q] : b;
+      return b;
+    };
+    uint64_t lb = lane_best(), km = 0;
     for (int rd = 0; rd < K; ++rd) {
-      float bv = cur;
-      int bl = lane;
-      wave_best(bv, bl);  // lowest lane on ties: a lane index works as the tie-break key
-      if (lane == 0) s_wk[w * TK_MAX + rd] = bv;
-      if (lane == bl) cur = -INFINITY;
+      km = wave_max_key(lb);
+      if (km == lb) {  // the winning thread's lane (keys are distinct) drops it
+        const int wq = (int)~(uint32_t)km >> 6;
+#pragma unroll
+        for (int q = 0; q < TR_WAVES; ++q) lk[q] = q == wq ? 0 : lk[q];
+        lb = lane_best();
+      }
+    }
+    if (lane == 0) {
+      float tv;
+      int ti;
+      vi_unkey(km, tv, ti);
+      s_t = tv;
     }
   }
   __syncthreads();
-  float t;
-  {
-    // every wave ranks the TR_WAVES * K maxima (at most 4 a lane)
-    float c[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = lane + 64 * q;
-      c[q] = j < TR_WAVES * K ? s_wk[(j / K) * TK_MAX + j % K] : -INFINITY;
-    }
-    t = -INFINITY;
-    for (int rd = 0; rd < K; ++rd) {
-      float bv = c[0];
-      int bq = 0;
-#pragma unroll
-      for (int q = 1; q < 4; ++q)
-        if (c[q] > bv) {
-          bv = c[q];
-          bq = q;
-        }
-      int bl = lane * 4 + bq;
-      wave_best(bv, bl);
-      t = bv;
-      if (lane == bl / 4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (q == bl % 4) c[q] = -INFINITY;
-      }
-    }
-  }
+  const float t = s_t;
   // 2. entries >= t into the LDS list
 #pragma unroll
   for (int u = 0; u < NV; ++u)
@@ -308,7 +317,26 @@ __global__ __launch_bounds__(TR_THREADS) void topk_row_kernel(int V, const float
     }
   __syncthreads();
   const int n = s_cnt;
-  // 3. K rounds, each over the entries strictly after the previous winner
+  // 3. K rounds of a maximum over the list
+  if (n <= 64) {
+    if (w != 0) return;
+    const float cv = lane < n ? s_cv[lane] : -INFINITY;
+    const int ci = lane < n ? s_ci[lane] : 0;
+    uint64_t k = lane < n ? vi_key(cv, ci) : 0;
+    for (int rd = 0; rd < K; ++rd) {
+      const uint64_t km = wave_max_key(k);
+      if (km != 0 && k == km) {  // the winner writes its own entry and drops out
+        idx[(size_t)row * K + rd] = ci;
+        if (val) val[(size_t)row * K + rd] = cv;
+        k = 0;
+      } else if (km == 0 && lane == 0) {  // fewer than K entries (rows of NaN)
+        idx[(size_t)row * K + rd] = 0;
+        if (val) val[(size_t)row * K + rd] = -INFINITY;
+      }
+    }
+    return;
+  }
+  // ... each round over the entries strictly after the previous winner
   float pv = INFINITY;
   int pi = -1;
   if (n <= TR_CAP) {
