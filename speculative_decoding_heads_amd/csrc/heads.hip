@@ -7,13 +7,14 @@
 //   1. z = h + SiLU(W1 h) for all heads at once (W1 stacked [H*d, d]) with the
 //      residual fused into the product's epilogue, z stored in the input dtype;
 //   2. logits[b, k, :] = W2[k] z[b, k] as H batched products (fp32 out);
-//   3. top-K per (b, k) row: for up to 768 rows of at most 32768 entries, one
+//   3. top-K per (b, k) row: for rows of at most 32768 entries, one
 //      1024-thread workgroup per row (threshold from the thread maxima, the few
-//      entries above it compacted in LDS, K selection rounds over them); else
-//      in two stages: one wave per vocabulary chunk keeps a sorted per-lane
+//      entries above it compacted in LDS, K selection rounds over them); for
+//      longer rows in two stages: one wave per vocabulary chunk keeps a sorted per-lane
 //      register list, then K rounds of a wave-wide (value desc, index asc)
 //      maximum pop the chunk's K best; one wave per row merges the chunks'
 //      candidates the same way.
+#include <limits.h>
 #include <stdlib.h>
 
 #include "common.h"
@@ -447,13 +448,14 @@ extern "C" int medusa_topk_rows(int M, int V, const float* x, int K, int32_t* id
                  topk_ws(M, V, K));
   const int vec4 = V % 4 == 0 && ((uintptr_t)x & 15) == 0;
   const int nv = (V + 4 * TR_THREADS - 1) / (4 * TR_THREADS);
-  // One workgroup per row reads a row at one CU's rate, so with many rows the
-  // two-stage path (each row spread over many waves) wins: measured at V 32000,
-  // 17 vs 26 us at 4 rows, 38 vs 46 us at 512, 127 vs 99 us at 2048.
-  // MEDUSA_TOPK_ROW_MAX_M overrides the 768-row limit (tuning runs).
+  // One workgroup per row for rows of at most 32768 entries: measured at V 32000
+  // and K 10 against the two-stage path (each row spread over many waves),
+  // 11 vs 26 us at 4 rows, 25 vs 47 us at 512, 51 vs 63 us at 1024 and 96 vs
+  // 108 us at 2048.  MEDUSA_TOPK_ROW_MAX_M sends larger row counts to the
+  // two-stage path (tuning runs).
   static const int e_rows = [] {
     const char* e = getenv("MEDUSA_TOPK_ROW_MAX_M");
-    return e ? atoi(e) : 768;
+    return e ? atoi(e) : INT_MAX;
   }();
   if (nv <= TR_MAX_NV && M <= e_rows) {
 #define TR_LAUNCH(NVV) \

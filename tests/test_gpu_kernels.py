@@ -331,20 +331,25 @@ def test_topk_rows_many_rows(dev, M, V):
     assert np.array_equal(to_np(val), np.take_along_axis(x, want, -1))
 
 
-@pytest.mark.parametrize("V,K", [(32000, 10), (32001, 16), (32768, 1), (4097, 10)])
+# rows of at most 32768 entries take the one-workgroup-per-row kernel, longer ones
+# (65537, and 128256 as in a 128k vocabulary) the two-stage path
+@pytest.mark.parametrize("V,K", [(32000, 10), (32001, 16), (32768, 1), (4097, 10), (65537, 16), (128256, 10)])
 def test_topk_rows_plateaus_and_full_vocab(dev, V, K):
     """Rows of a vocabulary's length: a plain random row, a row of one repeated value
-    (every entry ties at the threshold, more than the candidate list holds) and a
-    plateau with a few larger entries; the exact (value desc, index asc) top K."""
+    (every entry ties at the threshold, more than the candidate list holds), a
+    plateau with a few larger entries, half-integers, and -0 / +0 ties on top of a
+    row of -1; the exact (value desc, index asc) top K (-0 ties with +0)."""
     import torch
     from speculative_decoding_heads_amd import api
     say("topk rows plateaus V", V, "K", K)
     rng = np.random.default_rng(V + K)
-    x = np.zeros((4, V), np.float32)
+    x = np.zeros((5, V), np.float32)
     x[0] = rng.standard_normal(V)
     x[1] = 0.25
     x[2, rng.choice(V, 5, replace=False)] = 1.0
     x[3] = rng.integers(-3, 3, size=V) / 2.0
+    x[4] = -1.0
+    x[4, [7, 3, 11, 5, 2]] = [-0.0, 0.0, -0.0, 0.0, -0.0]
     idx, val = api.topk_rows(torch.from_numpy(x).to(dev), K)
     torch.cuda.synchronize()
     want = topk_desc(x, K)
