@@ -117,10 +117,23 @@ __global__ __launch_bounds__(kStatThreads) void node_stats_kernel(const float* _
     s_f[w] = z;
   }
   __syncthreads();
+  // wave 0 merges the waves' partials in wave order and shares the result (the
+  // sixteen waves doing the same merge would share the four SIMDs)
+  if (w == 0) {
+    bv = s_v[0];
+    bi = s_i[0];
+    z = s_f[0];
+    for (int j = 1; j < kStatThreads / 64; ++j) merge(s_v[j], s_i[j], s_f[j]);
+    if (lane == 0) {
+      s_v[0] = bv;
+      s_i[0] = bi;
+      s_f[0] = z;
+    }
+  }
+  __syncthreads();
   bv = s_v[0];
   bi = s_i[0];
   z = s_f[0];
-  for (int j = 1; j < kStatThreads / 64; ++j) merge(s_v[j], s_i[j], s_f[j]);
   if (bi == 0x7fffffff) bi = 0;  // all NaN row: report token 0
   if (!typical) {
     if (tid == 0) out[(size_t)b * T + u] = NodeStat{bi, bv, 0.f, 0.f};
