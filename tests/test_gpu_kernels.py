@@ -337,19 +337,25 @@ def test_topk_rows_many_rows(dev, M, V):
 def test_topk_rows_plateaus_and_full_vocab(dev, V, K):
     """Rows of a vocabulary's length: a plain random row, a row of one repeated value
     (every entry ties at the threshold, more than the candidate list holds), a
-    plateau with a few larger entries, half-integers, and -0 / +0 ties on top of a
-    row of -1; the exact (value desc, index asc) top K (-0 ties with +0)."""
+    plateau with a few larger entries, half-integers, -0 / +0 ties on top of a
+    row of -1 (5 of them, and 30 spread out: a short candidate list of ties), and
+    100 equal maxima on a random row (a candidate list longer than a wave); the
+    exact (value desc, index asc) top K (-0 ties with +0)."""
     import torch
     from speculative_decoding_heads_amd import api
     say("topk rows plateaus V", V, "K", K)
     rng = np.random.default_rng(V + K)
-    x = np.zeros((5, V), np.float32)
+    x = np.zeros((7, V), np.float32)
     x[0] = rng.standard_normal(V)
     x[1] = 0.25
     x[2, rng.choice(V, 5, replace=False)] = 1.0
     x[3] = rng.integers(-3, 3, size=V) / 2.0
     x[4] = -1.0
     x[4, [7, 3, 11, 5, 2]] = [-0.0, 0.0, -0.0, 0.0, -0.0]
+    x[5] = -1.0
+    x[5, rng.choice(V, 30, replace=False)] = np.where(np.arange(30) % 2 == 0, -0.0, 0.0)
+    x[6] = rng.standard_normal(V)
+    x[6, rng.choice(V, 100, replace=False)] = 10.0
     idx, val = api.topk_rows(torch.from_numpy(x).to(dev), K)
     torch.cuda.synchronize()
     want = topk_desc(x, K)
