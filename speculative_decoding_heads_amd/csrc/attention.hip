@@ -206,9 +206,12 @@ MfmaPlan mfma_plan_nw(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint, int
 // all R query rows of its KV head (R x Dh x 4 bytes, at 4 tiles a split about
 // what the split reads of K/V) that the merge reads back, and fewer waves mean
 // more 32-row chunks, each streaming the same K/V again.  Measured on MI355X
-// over batch 1 and 8, 8 and 32 KV heads x 128, prefixes 1k-64k and every
-// (waves, splits) pair: within 1 % of the best pair summed over the cases, the
-// worst case 15 % off (batch 1, 8 KV heads, prefix 8k).  MEDUSA_ATTN_WAVES =
+// over batch 1, 2, 4 and 8, 8 and 32 KV heads x 128, prefixes 1k-64k and every
+// (waves, splits) pair: within 0.5 % of the best pair summed over the 30
+// cases, the worst 15-19 % off (batch 1 / prefix 8k and batch 2 / prefix 4k
+// at 8 KV heads, where 4 waves and 8 tiles a split beat 2 waves and 16).  A
+// cost model (tiles a split times a per-tile time by rows, plus the merge's
+// partial bytes) ranks the same cases as well overall.  MEDUSA_ATTN_WAVES =
 // 2 | 4 | 8 forces a width.
 MfmaPlan mfma_plan(int B, int T, int Hq, int Hkv, int Dh, int64_t L_hint) {
   const int forced = attn_stream_waves_forced();
