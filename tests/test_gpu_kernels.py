@@ -102,6 +102,38 @@ def test_posterior_typical_extremes(dev):
     assert to_np(nr).tolist() == lg[:, 0].argmax(1).tolist()
 
 
+@pytest.mark.parametrize("V,off", [(6000, 0), (12004, 0), (16388, 0), (32001, 0), (40000, 0), (8000, 1)])
+@pytest.mark.parametrize("mode", [GREEDY, TYPICAL])
+def test_posterior_row_length_variants(dev, V, off, mode):
+    """Row lengths that take each register-set size of the per-node statistics (1024 threads
+    holding 1, 2, 4 or 8 four-float vectors; V 6000, 12004 and 16388 fill the last set only in
+    part) and the scalar path (V % 4 != 0, V > 32768, or a row base that is not 16-byte
+    aligned: ``off`` floats into the buffer).  Greedy: every candidate is its parent's argmax,
+    so every path must be accepted to its full depth; typical: the oracle's outcome, with the
+    usual near-tie allowance."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    choices = seeded_tree_choices(0)
+    tree = api.Tree(choices)
+    ot = tree_buffers(choices)
+    T, B = ot["T"], 3
+    say("evaluate_posterior V", V, "offset", off, "mode", mode)
+    rng = np.random.default_rng(V + 7 * off + 13 * mode)
+    lg, toks = _posterior_case(rng, ot, B, V, mode, match_p=1.0 if mode == GREEDY else 0.7, scale=2.0)
+    buf = torch.empty(B * T * V + off, dtype=torch.float32, device=dev)
+    buf[off:] = torch.from_numpy(lg.ravel()).to(dev)
+    lgd = buf[off:].view(B, T, V)
+    assert (lgd.data_ptr() % 16 != 0) == (off % 4 != 0)
+    tau, eps, delta = 0.7, 0.09, 0.3
+    best, a, sel, nr = api.evaluate_posterior(tree, lgd, torch.from_numpy(toks).to(dev), mode, tau, eps, delta)
+    torch.cuda.synchronize()
+    got = np.stack([to_np(x) for x in (best, a, sel, nr)], 1)
+    if mode == GREEDY:
+        assert got[:, 1].tolist() == [ot["D"]] * B
+    near = sum(posterior_outcome(ot, lg[b], toks[b], mode, tau, eps, delta, got[b]) for b in range(B))
+    assert near <= 1
+
+
 @pytest.mark.parametrize("dtype_name", ["bf16", "fp32"])
 def test_kv_compact_bit_exact(dev, dtype_name):
     import torch

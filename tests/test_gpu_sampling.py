@@ -54,6 +54,34 @@ def test_sample_tokens_vs_oracle(dev, kind, V, scale):
     assert np.array_equal(again, got)
 
 
+@pytest.mark.parametrize("kind", [SAMPLE_TYPICAL, SAMPLE_NUCLEUS])
+@pytest.mark.parametrize("V,off", [(6000, 0), (12004, 0), (40000, 0), (8000, 1)])
+def test_sample_tokens_row_length_variants(dev, kind, V, off):
+    """Row lengths that take the draw kernel's 2- and 4-vector register sets (12004 fills the
+    last set in part) and its scalar path (V > 32768, or rows whose base is not 16-byte
+    aligned: ``off`` floats into the buffer)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("sample_tokens kind", kind, "V", V, "offset", off)
+    rng = np.random.default_rng(3 * V + kind + off)
+    M = 48
+    lg = (rng.standard_normal((M, V)) * 2.0).astype(np.float32)
+    pos = rng.integers(0, 100000, M).astype(np.int32)
+    seq = rng.integers(0, 8, M).astype(np.int32)
+    sm = _sampling(kind, seed=91)
+    buf = torch.empty(M * V + off, dtype=torch.float32, device=dev)
+    buf[off:] = torch.from_numpy(lg.ravel()).to(dev)
+    lgd = buf[off:].view(M, V)
+    assert (lgd.data_ptr() % 16 != 0) == (off % 4 != 0)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    got = to_np(api.sample_tokens(lgd, sm, d(pos), seq_id=d(seq)))
+    torch.cuda.synchronize()
+    want, margins = draw_rows(lg, kind, sm["temperature"], sm["eps"], sm["delta"], sm["top_p"], sm["seed"], seq, pos)
+    diff = np.flatnonzero(got != want)
+    assert all(margins[i] < NEAR for i in diff), [(int(i), int(got[i]), int(want[i]), margins[i]) for i in diff]
+    assert len(diff) <= 2
+
+
 def _node_draws(dev, lg, tree_pos, sm):
     """GPU draws at every node of every sequence (medusa_sample_tokens), [B, T]."""
     import torch
