@@ -237,7 +237,11 @@ def test_heads_topk_fp32_small(dev):
                                    (64, 32000, 256), (48, 5000, 1024),
                                    # few rows with K % 64 != 0: the register-staged 64-row-tile kernel,
                                    # rows past M re-reading the last one
-                                   (1, 3000, 1056), (5, 4096, 96), (17, 700, 1056)])
+                                   (1, 3000, 1056), (5, 4096, 96), (17, 700, 1056),
+                                   # N % 4 != 0: every epilogue's element-by-element stores (direct-load
+                                   # tiles; the split-K reduction at M 1; register-staged; square tiles)
+                                   (64, 1001, 256), (8, 999, 512), (1, 4095, 4096), (5, 4099, 96),
+                                   (300, 1003, 512)])
 def test_gemm_bf16(dev, M, N, K):
     import torch
     from speculative_decoding_heads_amd import api
@@ -281,6 +285,38 @@ def test_gemm_epilogues(dev, dtype_name, M):
     out = api.gemm(gA, to_dev(Wsq, tdt, dev), EPI_SILU_RESID_A)
     z = A.astype(np.float64) @ Wsq.astype(np.float64).T
     assert_close(to_np(out), np.concatenate([A, A], 1) + silu(z), what="silu_resid", **tol)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [5, 64, 260])
+def test_gemm_epilogues_odd_widths(dev, M):
+    """bf16 store and residual epilogues at N 1001 and SwiGLU at N 514 (257 outputs a
+    row): output rows whose stride and width are not multiples of 4 take the
+    element-by-element stores; M 260 takes the square-tile kernel."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import EPI_RESID, EPI_STORE, EPI_SWIGLU
+    from workloads import bf16_round
+    say("gemm odd-width epilogues M", M)
+    tol = dict(rtol=2e-2, atol=1e-2)
+    rng = np.random.default_rng(M + 3)
+    K = 256
+    A = bf16_round(rng.standard_normal((M, K)).astype(np.float32))
+    W = bf16_round((rng.standard_normal((1001, K)) * 0.05).astype(np.float32))
+    R = bf16_round(rng.standard_normal((M, 1001)).astype(np.float32))
+    acc = A.astype(np.float64) @ W.astype(np.float64).T
+    gA = to_dev(A, torch.bfloat16, dev)
+    gW = to_dev(W, torch.bfloat16, dev)
+    out = api.gemm(gA, gW, EPI_STORE)
+    assert_close(to_np(out), acc, what="store", **tol)
+    gR = to_dev(R, torch.bfloat16, dev)
+    out = api.gemm(gA, gW, EPI_RESID, out=gR.clone(), R=gR)
+    assert_close(to_np(out), acc + R, what="resid", **tol)
+    W2 = bf16_round((rng.standard_normal((514, K)) * 0.05).astype(np.float32))
+    acc2 = A.astype(np.float64) @ W2.astype(np.float64).T
+    out = api.gemm(gA, to_dev(W2, torch.bfloat16, dev), EPI_SWIGLU)
+    assert tuple(out.shape) == (M, 257)
+    assert_close(to_np(out), silu(acc2[:, 0::2]) * acc2[:, 1::2], what="swiglu", **tol)
     torch.cuda.synchronize()
 
 
@@ -357,6 +393,28 @@ def test_topk_rows_many_rows(dev, M, V):
     rng = np.random.default_rng(M)
     x = rng.integers(-50, 50, size=(M, V)).astype(np.float32) / 8.0
     idx, val = api.topk_rows(torch.from_numpy(x).to(dev), 10)
+    torch.cuda.synchronize()
+    want = topk_desc(x, 10)
+    assert np.array_equal(to_np(idx), want)
+    assert np.array_equal(to_np(val), np.take_along_axis(x, want, -1))
+
+
+@pytest.mark.parametrize("V", [8000, 40000])
+def test_topk_rows_unaligned_rows(dev, V):
+    """Rows whose base is not 16-byte aligned (one float into the buffer) are read as
+    scalars: the one-workgroup-per-row kernel (V 8000) and the two-stage path (V 40000);
+    values from a small set so that ties are common."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("topk rows unaligned V", V)
+    rng = np.random.default_rng(V + 1)
+    M = 6
+    x = rng.integers(-50, 50, size=(M, V)).astype(np.float32) / 8.0
+    buf = torch.empty(M * V + 1, dtype=torch.float32, device=dev)
+    buf[1:] = torch.from_numpy(x.ravel()).to(dev)
+    xd = buf[1:].view(M, V)
+    assert xd.data_ptr() % 16 != 0
+    idx, val = api.topk_rows(xd, 10)
     torch.cuda.synchronize()
     want = topk_desc(x, 10)
     assert np.array_equal(to_np(idx), want)
