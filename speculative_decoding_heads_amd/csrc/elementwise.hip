@@ -1,8 +1,8 @@
 // Row-wise kernels of the verify forward: RMSNorm, rotary split of the fused
 // Q/K/V projection into the query tensor and the tree K/V side buffers,
 // embedding gather, row gather (the selected node's hidden state, which the
-// page "大模型推理 memory bandwidth bound (5) - Medusa" hands to the next round's
-// heads in section 二.7) and row argmax (the greedy root of section 二.4).
+// page "大模型推理 memory bandwidth bound (5) - Medusa" hands to the next decode
+// step's heads in section 二.7) and row argmax (the greedy root of section 二.4).
 #include "common.h"
 #include "medusa_model.h"
 
