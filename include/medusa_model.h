@@ -132,6 +132,9 @@ typedef struct medusa_model {
  * (uint64 [T], device) among the new tokens.  Writes the new tokens' K/V to
  * Kt/Vt [n_layers, B, Hkv, T, Dh], logits [B, T, V] (fp32) and the final-normed
  * hidden state h [B, T, d] (dtype).  L_hint as in tree_attention.
+ * Model shapes (checked first by every call that takes a model, which then
+ * returns MEDUSA_ERR_UNSUPPORTED with nothing launched): head_dim <= 128; bf16
+ * also needs d, n_heads * head_dim and ffn multiples of 32 and d <= 8192.
  */
 size_t medusa_forward_workspace_size(const medusa_model* m, int B, int T, int64_t L_hint);
 int medusa_forward(const medusa_model* m, int B, int T, const int32_t* tokens, const int32_t* pos, const void* Kc,

@@ -116,6 +116,15 @@ int check_model(const medusa_model* m) {
                      m->n_heads % m->n_kv_heads == 0 && m->head_dim > 0 && m->head_dim % 2 == 0 && m->ffn > 0 &&
                      m->vocab > 0,
                  MEDUSA_ERR_ARG, "model: bad dimensions");
+  // shapes every kernel of the forward takes, checked before anything is launched:
+  // attention heads of at most 128; bf16 products step K by 32 (K = d, Hq * Dh and
+  // ffn) and the residual norms hold a row of at most 8192
+  MEDUSA_REQUIRE(m->head_dim <= 128, MEDUSA_ERR_UNSUPPORTED, "model: head_dim %d > 128", m->head_dim);
+  MEDUSA_REQUIRE(m->dtype != MEDUSA_BF16 || (m->d % 32 == 0 && (m->n_heads * m->head_dim) % 32 == 0 &&
+                                             m->ffn % 32 == 0 && m->d <= 8192),
+                 MEDUSA_ERR_UNSUPPORTED,
+                 "model: bf16 needs d, n_heads * head_dim and ffn multiples of 32 and d <= 8192 (d %d, %d, ffn %d)",
+                 m->d, m->n_heads * m->head_dim, m->ffn);
   MEDUSA_REQUIRE(m->layers && m->embed && m->final_norm && m->lm_head && m->rope_cos && m->rope_sin &&
                      m->rope_max_pos > 0,
                  MEDUSA_ERR_ARG, "model: null weight pointer");

@@ -120,3 +120,26 @@ def test_sampling_calls_errors():
             ["null pointer"])
     _expect(lib.evaluate_posterior_sampled(None, 2, 100, FAKE, FAKE, FAKE, C.byref(good), FAKE, FAKE, FAKE, FAKE,
                                            FAKE, 1 << 20, None), ARG, ["null tree"])
+
+
+def _forward_with(**over):
+    """medusa_forward on a bf16 model description with fake device pointers: shape
+    errors are reported before any device work."""
+    from speculative_decoding_heads_amd._lib import LayerWeights, ModelDesc
+    dims = dict(dtype=1, n_layers=1, d=512, n_heads=8, n_kv_heads=4, head_dim=64, ffn=1024, vocab=100)
+    dims.update(over)
+    layer = LayerWeights(*([FAKE.value] * 6))
+    m = ModelDesc(dims["dtype"], dims["n_layers"], dims["d"], dims["n_heads"], dims["n_kv_heads"], dims["head_dim"],
+                  dims["ffn"], dims["vocab"], 1e-6, FAKE.value, FAKE.value, FAKE.value, C.pointer(layer),
+                  FAKE.value, FAKE.value, 256, 0, None, None)
+    return _lib().medusa_forward(C.byref(m), 1, 8, FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, 1 << 30, None)
+
+
+def test_forward_model_shape_errors():
+    _expect(_forward_with(ffn=1000), UNSUP, ["multiples of 32", "ffn 1000"])
+    _expect(_forward_with(d=520), UNSUP, ["multiples of 32", "d 520"])
+    _expect(_forward_with(d=8224), UNSUP, ["d <= 8192"])
+    _expect(_forward_with(n_heads=3, n_kv_heads=1, head_dim=48), UNSUP, ["multiples of 32"])
+    _expect(_forward_with(head_dim=256, n_heads=2, n_kv_heads=2), UNSUP, ["head_dim 256 > 128"])
+    _expect(_forward_with(n_heads=6, n_kv_heads=4), ARG, ["bad dimensions"])

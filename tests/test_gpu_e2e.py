@@ -250,12 +250,12 @@ def _forward_parity(dev, model, params, tok, pos, gKc, gVc, seq, tree, ot, Lmax,
     assert e2e <= E2E_LOGIT_ATOL, e2e
 
 
-def _small_bf16_model(seed, heads_kv_dim=(8, 4, 64)):
+def _small_bf16_model(seed, heads_kv_dim=(8, 4, 64), d_model=512, ffn_dim=1024):
     class Cfg:
         n_layers = 2
-        d = 512
+        d = d_model
         n_heads, n_kv_heads, head_dim = heads_kv_dim
-        ffn = 1024
+        ffn = ffn_dim
         vocab = 2048
         n_medusa = 4
         rope_theta = 10000.0
@@ -285,6 +285,37 @@ def test_bf16_forward_vs_oracle(dev, heads_kv_dim, B, tree_name):
     tree = api.Tree(choices)
     ot = tree_buffers(choices)
     rng = np.random.default_rng(4)
+    L, Lmax = 150, 192
+    NL, Hkv, Dh = Cfg.n_layers, Cfg.n_kv_heads, Cfg.head_dim
+    from workloads import bf16_round
+    Kc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
+    Vc = bf16_round(rng.standard_normal((NL, B, Hkv, Lmax, Dh)).astype(np.float32))
+    seq = np.array([L, L - 37][:B], np.int32)
+    toks = rng.integers(0, Cfg.vocab, (B, ot["T"])).astype(np.int32)
+    pos = (seq[:, None] + ot["depth"][None, :]).astype(np.int32)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    _forward_parity(dev, model, params, d(toks), d(pos), to_dev(Kc, torch.bfloat16, dev),
+                    to_dev(Vc, torch.bfloat16, dev), d(seq), tree, ot, Lmax, Kc, Vc)
+
+
+# Uneven shapes: 6 query heads on 2 KV heads (groups of 3), one KV head for 4 query
+# heads, 7 heads of 64 on a hidden size of 448; SwiGLU widths 1056 and 1000 (K % 64 != 0
+# for the down projection: the register-staged product with the fused residual norm)
+@pytest.mark.parametrize("heads_kv_dim,d_model,ffn_dim,B,tree_name", [((6, 2, 64), 384, 1056, 1, "page"),
+                                                                      ((4, 1, 128), 512, 1056, 2, "seeded24"),
+                                                                      ((7, 7, 64), 448, 1120, 1, "page")])
+def test_bf16_forward_uneven_shapes(dev, heads_kv_dim, d_model, ffn_dim, B, tree_name):
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd.model import Model
+    say("e2e bf16 forward, uneven shapes", heads_kv_dim, "d", d_model, "ffn", ffn_dim, "batch", B, tree_name)
+    (params, heads), Cfg = _small_bf16_model(5, heads_kv_dim, d_model, ffn_dim)
+    P, H = _upload(params, heads, torch.bfloat16, dev)
+    model = Model(P, H, max_pos=1024)
+    choices = {"page": PAGE_TREE_CHOICES, "seeded24": seeded_tree_choices(3, n_nodes=23)}[tree_name]
+    tree = api.Tree(choices)
+    ot = tree_buffers(choices)
+    rng = np.random.default_rng(6)
     L, Lmax = 150, 192
     NL, Hkv, Dh = Cfg.n_layers, Cfg.n_kv_heads, Cfg.head_dim
     from workloads import bf16_round
