@@ -208,6 +208,48 @@ def test_tiny_fp32_sampled_medusa_equals_plain_sampled_decoding(dev, kind, force
         assert all((a == 2).all() for a in accs)
 
 
+def _gpu_sampled_fused_run(dev, params, heads, choices, prompt, n_steps, sm):
+    """As _gpu_sampled_run, with the fused draft + verify step (heads on every node)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    from speculative_decoding_heads_amd._lib import SAMPLED
+    from speculative_decoding_heads_amd.model import Model, State, init_topk_carry, prefill, step_fused
+    P, H = _upload(params, heads, dev)
+    model = Model(P, H, max_pos=1024)
+    tree = api.Tree(choices)
+    B = prompt.shape[0]
+    st = State(model, B, 256, 128, sampling=sm)
+    prefill(model, st, torch.from_numpy(prompt.astype(np.int32)).to(dev))
+    carry = init_topk_carry(model, tree, st)
+    accs = []
+    for s in range(n_steps):
+        step_fused(model, tree, st, carry, SAMPLED, L_hint=256)
+        accs.append(to_np(st.accept_len).copy())
+    torch.cuda.synchronize()
+    assert int(to_np(st.err)[0]) == 0
+    n, toks = to_np(st.n_out), to_np(st.out_tokens)
+    return [toks[b, : n[b]].tolist() for b in range(B)], accs
+
+
+@pytest.mark.parametrize("kind", [SAMPLE_TYPICAL, SAMPLE_NUCLEUS])
+def test_tiny_fp32_fused_sampled_equals_step(dev, kind):
+    """The fused draft + verify step with sampled acceptance: the fp32 heads give the
+    same top-K on every node as on the selected node alone, and the draws depend only
+    on (sequence, position), so tokens and per-step accepted lengths equal the plain
+    step's, and the tokens equal plain sampled decoding in the oracle."""
+    say("e2e tiny fp32 fused sampled kind", kind)
+    params, heads = tiny_model(0)
+    prompt = prompt_tokens(101, 2, TinyConfig.prompt_len, TinyConfig.vocab)
+    sm = _sampling(kind, seed=77)
+    fused, facc = _gpu_sampled_fused_run(dev, params, heads, TWO_HEAD_CHOICES, prompt, 10, sm)
+    plain_step, pacc = _gpu_sampled_run(dev, params, heads, TWO_HEAD_CHOICES, prompt, 10, sm)
+    assert fused == plain_step
+    assert all(np.array_equal(a, b) for a, b in zip(facc, pacc))
+    ref = plain_sampled_decode(params, prompt, max(len(f) for f in fused) + 1, 256, sm)
+    for b in range(2):
+        assert fused[b] == ref[b, : len(fused[b])].tolist(), "fused sampled medusa != plain sampled decoding"
+
+
 def test_bf16_sampled_step_state(dev):
     """A bf16 sampled step (page tree, typical draws) leaves the state the non-fast
     rule gives on the same forward's logits: acceptance, compaction, next root."""
