@@ -399,6 +399,55 @@ def test_topk_rows_many_rows(dev, M, V):
     assert np.array_equal(to_np(val), np.take_along_axis(x, want, -1))
 
 
+@pytest.mark.parametrize("V", [1, 3, 17, 64, 65, 100])
+def test_topk_and_argmax_short_rows(dev, V):
+    """Rows far shorter than a workgroup (most threads hold only padding): random, all
+    -inf (the top K are the first K indices), one finite entry among -inf, constant,
+    and small integers (many ties); top-K with K = min(V, 10) and the row argmax."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("topk / argmax short rows V", V)
+    rng = np.random.default_rng(V + 5)
+    K = min(V, 10)
+    x = np.zeros((5, V), np.float32)
+    x[0] = rng.standard_normal(V)
+    x[1] = -np.inf
+    x[2] = -np.inf
+    x[2, V // 2] = -3.0
+    x[3] = 0.5
+    x[4] = rng.integers(-2, 2, size=V)
+    g = torch.from_numpy(x).to(dev)
+    idx, val = api.topk_rows(g, K)
+    am = api.argmax_rows(g)
+    torch.cuda.synchronize()
+    want = topk_desc(x, K)
+    assert np.array_equal(to_np(idx), want)
+    assert np.array_equal(to_np(val), np.take_along_axis(x, want, -1))
+    assert to_np(am).tolist() == want[:, 0].tolist()
+
+
+@pytest.mark.parametrize("V", [2, 5])
+@pytest.mark.parametrize("mode", [GREEDY, TYPICAL])
+def test_posterior_tiny_vocabulary(dev, V, mode):
+    """Vocabularies of 2 and 5 tokens: nearly every thread of the per-node statistics
+    holds padding; the outcome equals the oracle's (counted near-ties)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("evaluate_posterior tiny V", V, "mode", mode)
+    ot = tree_buffers(PAGE_TREE_CHOICES)
+    tree = api.Tree(PAGE_TREE_CHOICES)
+    rng = np.random.default_rng(V + 31 * mode)
+    B = 4
+    lg, toks = _posterior_case(rng, ot, B, V, mode, match_p=0.8, scale=1.5)
+    tau, eps, delta = 0.7, 0.09, 0.3
+    best, a, sel, nr = api.evaluate_posterior(tree, torch.from_numpy(lg).to(dev), torch.from_numpy(toks).to(dev),
+                                              mode, tau, eps, delta)
+    torch.cuda.synchronize()
+    got = np.stack([to_np(x) for x in (best, a, sel, nr)], 1)
+    near = sum(posterior_outcome(ot, lg[b], toks[b], mode, tau, eps, delta, got[b]) for b in range(B))
+    assert near <= 1
+
+
 @pytest.mark.parametrize("V", [8000, 40000])
 def test_topk_rows_unaligned_rows(dev, V):
     """Rows whose base is not 16-byte aligned (one float into the buffer) are read as

@@ -55,6 +55,30 @@ def test_sample_tokens_vs_oracle(dev, kind, V, scale):
 
 
 @pytest.mark.parametrize("kind", [SAMPLE_TYPICAL, SAMPLE_NUCLEUS])
+@pytest.mark.parametrize("V", [1, 2, 5])
+def test_sample_tokens_tiny_vocabulary(dev, kind, V):
+    """Vocabularies of 1, 2 and 5 tokens (one token: every draw is token 0)."""
+    import torch
+    from speculative_decoding_heads_amd import api
+    say("sample_tokens tiny V", V, "kind", kind)
+    rng = np.random.default_rng(7 * V + kind)
+    M = 64
+    lg = (rng.standard_normal((M, V)) * 1.5).astype(np.float32)
+    pos = rng.integers(0, 100000, M).astype(np.int32)
+    seq = rng.integers(0, 8, M).astype(np.int32)
+    sm = _sampling(kind, seed=5)
+    d = lambda x: torch.from_numpy(x).to(dev)
+    got = to_np(api.sample_tokens(d(lg), sm, d(pos), seq_id=d(seq)))
+    torch.cuda.synchronize()
+    want, margins = draw_rows(lg, kind, sm["temperature"], sm["eps"], sm["delta"], sm["top_p"], sm["seed"], seq, pos)
+    if V == 1:
+        assert got.tolist() == [0] * M
+    diff = np.flatnonzero(got != want)
+    assert all(margins[i] < NEAR for i in diff), [(int(i), int(got[i]), int(want[i]), margins[i]) for i in diff]
+    assert len(diff) <= 2
+
+
+@pytest.mark.parametrize("kind", [SAMPLE_TYPICAL, SAMPLE_NUCLEUS])
 @pytest.mark.parametrize("V,off", [(6000, 0), (12004, 0), (40000, 0), (8000, 1)])
 def test_sample_tokens_row_length_variants(dev, kind, V, off):
     """Row lengths that take the draw kernel's 2- and 4-vector register sets (12004 fills the
